@@ -1,0 +1,209 @@
+/*
+ * ringattn.h -- C ABI of the MI355X (gfx950) blockwise ring-attention library.
+ *
+ * One GPU's share of ring attention / context parallelism: the head-tail
+ * (zigzag) sequence partition, the interleaved KV-cache slot mapping, one
+ * (Q chunk, KV block) ring step of blockwise attention that returns the
+ * partial output O with its log-sum-exp (LSE), the LSE merge of partials,
+ * and grouped-query decode over a sequence-sharded KV cache.
+ *
+ * Sources for the operations (web pages; section names given so a reader
+ * can find the passage):
+ *   [CP]   vLLM-Ascend developer guide, "Context Parallel (CP)" (v0.13.0):
+ *          "How it works / Block table", "Decode context parallel (DCP)",
+ *          "Prefill context parallel (PCP)" with its paragraphs on the
+ *          head-tail token partition, prefill, decode and chunked prefill.
+ *   [RA]   guijiagi.com tag page "Ring Attention": excerpts on the ring
+ *          topology and on the memory wall of plain attention (formula and
+ *          "key insight").
+ *   [VID]  video page "How Context Parallelism Splits Long Sequences Across
+ *          GPUs", chapter list (online softmax, double buffering, causal
+ *          masks).
+ *   [DIAG] Excalidraw diagram "Context Parallel (CP) / Ring Attention":
+ *          K/V rotate around the ring while local attention runs.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns a cp_status_t value (as int32_t).  On any
+ *     status other than CP_OK nothing has been written and nothing launched
+ *     (except CP_EHIP, reported after a launch failed).  A short detail
+ *     string for the calling thread is available from cp_last_error().
+ *   - The library never prints, never throws across this boundary, keeps no
+ *     global mutable state besides the thread-local error string, and
+ *     allocates no device memory: the caller owns every buffer.
+ *   - Host functions are synchronous and take host pointers.  Device
+ *     functions take device pointers (16-byte aligned, densely packed in the
+ *     layouts stated), are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream) and return after the launch.
+ *   - Integer sizes are int64_t where they can exceed 2^31; all device
+ *     offsets are computed in 64 bits.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RINGATTN_ABI_VERSION 1
+
+typedef enum {
+  CP_OK = 0,
+  CP_EINVAL = 1,        /* bad argument: null pointer, bad size, constraint violated */
+  CP_EDTYPE = 2,        /* dtype code not known */
+  CP_EUNSUPPORTED = 3,  /* valid request this build has no kernel for (head dims, group size) */
+  CP_EHIP = 4           /* HIP runtime reported an error at launch */
+} cp_status_t;
+
+typedef enum { CP_BF16 = 0, CP_F32 = 1 } cp_dtype_t;
+typedef enum { CP_MASK_NONE = 0, CP_MASK_CAUSAL = 1 } cp_mask_t;
+typedef enum { CP_CLASS_FULL = 0, CP_CLASS_DIAG = 1, CP_CLASS_SKIP = 2 } cp_class_t;
+
+/* RINGATTN_ABI_VERSION of the loaded library. */
+int32_t cp_abi_version(void);
+/* Static, human-readable name of a status code. */
+const char* cp_status_string(int32_t status);
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* cp_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * cp_partition -- head-tail (zigzag) token partition and restore index.
+ * [CP] "Prefill context parallel (PCP)", head-tail token partition.
+ *
+ * Each request of length L is padded at its tail to the smallest multiple
+ * of 2*cp_size, cut into 2*cp_size equal parts of c tokens, and rank r
+ * takes part r followed by part 2*cp_size-1-r.  Requests are processed in
+ * order and concatenated per rank.  Tokens are numbered globally, request
+ * after request; padding is -1.
+ *
+ *   seq_lens        [num_reqs] request lengths (>= 0), host.
+ *   rank            rank whose local list is produced, 0 <= rank < cp_size.
+ *   local_token_idx [*local_len] out: global token ids held by `rank`.
+ *   local_len       in: capacity of local_token_idx; out: entries needed.
+ *   restore_idx     [*restore_len] out: restore_idx[t] is the position of
+ *                   original token t in the rank-ordered concatenation of all
+ *                   ranks' local lists (what an all-gather produces).
+ *   restore_len     in: capacity; out: entries needed (= sum of seq_lens).
+ * Pass local_token_idx == NULL and restore_idx == NULL to query the two
+ * lengths only.  Either array may be NULL to skip it.  A capacity smaller
+ * than needed is CP_EINVAL.
+ * ---------------------------------------------------------------------- */
+int32_t cp_partition(const int64_t* seq_lens, int32_t num_reqs, int32_t cp_size, int32_t rank,
+                     int64_t* local_token_idx, int64_t* local_len,
+                     int64_t* restore_idx, int64_t* restore_len);
+
+/* ------------------------------------------------------------------------
+ * cp_slot_mapping -- interleaved virtual-block KV placement.
+ * [CP] "How it works / Block table".
+ *
+ * With W = pcp_size*dcp_size, a virtual block holds block_size*W tokens.
+ * For token position x:  vb = x / (block_size*W),  off = x % (block_size*W),
+ * lbi = off / interleave,  device = lbi % W,
+ * in_block = (lbi / W) * interleave + off % interleave,
+ * slot = block_table[vb] * block_size + in_block  (identity table if NULL).
+ *
+ *   positions   [n] token positions (>= 0), host.
+ *   block_table [block_table_len] physical block of each virtual block, or
+ *               NULL for the identity; every vb reached must be < len.
+ *   device_out  [n] out: device id in [0, W).
+ *   slot_out    [n] out: slot on that device.
+ * block_size % interleave != 0 is CP_EINVAL (the page requires it).
+ * ---------------------------------------------------------------------- */
+int32_t cp_slot_mapping(const int64_t* positions, int64_t n, int32_t block_size,
+                        int32_t interleave, int32_t pcp_size, int32_t dcp_size,
+                        const int32_t* block_table, int64_t block_table_len,
+                        int32_t* device_out, int64_t* slot_out);
+
+/* ------------------------------------------------------------------------
+ * cp_classify -- class of one (Q range, KV range) block pair.
+ * [VID] chapter on kernels, overlap and causal masks; [RA] ring topology.
+ *
+ * Queries sit at positions [q_pos0, q_pos0+sq), keys at [k_pos0, k_pos0+sk).
+ * Under CP_MASK_CAUSAL key k is visible to query q iff k <= q.
+ * *class_out = CP_CLASS_FULL if every pair is visible, CP_CLASS_SKIP if none
+ * is (or the block is empty), CP_CLASS_DIAG otherwise.
+ * ---------------------------------------------------------------------- */
+int32_t cp_classify(int64_t q_pos0, int64_t sq, int64_t k_pos0, int64_t sk, int32_t mask,
+                    int32_t* class_out);
+
+/* ------------------------------------------------------------------------
+ * ring_attn_step -- blockwise attention of one Q chunk against one KV block.
+ * [RA] memory-wall excerpt (softmax(Q K^T / sqrt(d)) V accumulated block by
+ * block with a running max and running sum) and ring-topology excerpt;
+ * [CP] DCP section (attn_output with attn_lse, combined by the LSE rule).
+ *
+ *   q     [batch, sq, hq, d_qk]   dtype (CP_BF16 or CP_F32), device.
+ *   k     [batch, sk, hkv, d_qk]  dtype, device.
+ *   v     [batch, sk, hkv, d_v]   dtype, device.
+ *   o     [batch, sq, hq, d_v]    float32, device, in/out.
+ *   lse   [batch, sq, hq]         float32, device, in/out; natural log of
+ *         sum_k exp(scale * q.k) over the visible keys.
+ *   class_out  optional host int32: the block pair's cp_class_t.
+ * Query row i is at absolute position q_pos0+i and key j at k_pos0+j; with
+ * CP_MASK_CAUSAL key j is visible to row i iff k_pos0+j <= q_pos0+i.  Query
+ * head h reads kv head h / (hq/hkv) (hq must be a multiple of hkv).
+ * accumulate == 0: o/lse are overwritten with this block's normalised
+ *   partial; rows that see no key get O = 0, LSE = -inf (a SKIP pair writes
+ *   that for every row).
+ * accumulate == 1: this block's partial is LSE-merged into the running
+ *   (o, lse) in place; a SKIP pair launches nothing.
+ * Supported (d_qk, d_v): (64,64), (128,128), (192,128); others are
+ * CP_EUNSUPPORTED.  bf16 runs on MFMA with float32 accumulation; float32
+ * inputs run a float32 vector path.
+ * ---------------------------------------------------------------------- */
+int32_t ring_attn_step(const void* q, const void* k, const void* v, int32_t dtype,
+                       int32_t batch, int64_t sq, int64_t sk, int32_t hq, int32_t hkv,
+                       int32_t d_qk, int32_t d_v, int64_t q_pos0, int64_t k_pos0,
+                       int32_t mask, float scale, int32_t accumulate,
+                       float* o, float* lse, int32_t* class_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * lse_merge -- combine n partial (O, LSE) results of the same rows.
+ * [CP] DCP section (output and LSE combined to update the result);
+ * [RA] memory-wall excerpt (running max and running sum).
+ *
+ *   o_parts   [n_parts, rows, d_v] float32, device.
+ *   lse_parts [n_parts, rows]      float32, device.
+ *   o_out     [rows, d_v]          float32 or bf16 (out_dtype), device.
+ *   lse_out   [rows]               float32, device, or NULL.
+ * With M = max_k LSE_k: LSE = M + ln sum_k exp(LSE_k - M) and
+ * O = sum_k exp(LSE_k - LSE) * O_k.  Rows whose parts are all -inf give
+ * O = 0, LSE = -inf.  d_v must be a multiple of 4 and at most 512.
+ * o_out may alias nothing in o_parts.
+ * ---------------------------------------------------------------------- */
+int32_t lse_merge(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows,
+                  int32_t d_v, void* o_out, int32_t out_dtype, float* lse_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * split_kv_decode -- one-token GQA decode over a sequence-sharded KV cache.
+ * [CP] "Decode context parallel (DCP)" and the PCP decode paragraph: each
+ * device attends with its slice of the KV cache, then the partial outputs
+ * and LSEs are combined (here: lse_merge with n_parts = n_shards).
+ *
+ *   q          [batch, hq, d_qk]                        dtype, device.
+ *   k_shards   [n_shards, batch, t_shard, hkv, d_qk]    dtype, device.
+ *   v_shards   [n_shards, batch, t_shard, hkv, d_v]     dtype, device.
+ *   shard_lens device int64 [n_shards*batch]: valid tokens of each
+ *              (shard, request), slots [0, len) (<= t_shard); NULL = t_shard.
+ *   o_parts    [n_shards, batch, hq, d_v] float32, device, out.
+ *   lse_parts  [n_shards, batch, hq]      float32, device, out.
+ *   workspace  device scratch of at least split_kv_decode_workspace(...)
+ *              bytes (may be NULL when that size is 0).
+ * The query attends to every valid token with no mask; the order of tokens
+ * inside a shard does not matter.  Only CP_BF16 with d_qk = d_v = 128 and
+ * 1 <= hq/hkv <= 16 is supported in this build.
+ * ---------------------------------------------------------------------- */
+size_t split_kv_decode_workspace(int32_t n_shards, int32_t batch, int32_t hq, int32_t hkv,
+                                 int32_t d_v, int64_t t_shard);
+int32_t split_kv_decode(const void* q, const void* k_shards, const void* v_shards, int32_t dtype,
+                        int32_t n_shards, int32_t batch, int64_t t_shard,
+                        const int64_t* shard_lens, int32_t hq, int32_t hkv, int32_t d_qk,
+                        int32_t d_v, float scale, float* o_parts, float* lse_parts,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RINGATTN_H */

@@ -1,0 +1,255 @@
+"""MI355X-native blockwise ring attention: thin Python binding of libringattn.so.
+
+Every function here only marshals arguments for the C ABI declared in
+``include/ringattn.h``; all the work runs in the library (host index code in
+C++, attention / merge / decode in HIP kernels for gfx950).  PyTorch is used
+for device memory and streams only.  Importing this package fails loudly
+when the library has not been built (``python -m ring_attention_02_amd.build``):
+there is no fallback implementation.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libringattn.so")
+
+CP_OK, CP_EINVAL, CP_EDTYPE, CP_EUNSUPPORTED, CP_EHIP = 0, 1, 2, 3, 4
+CP_BF16, CP_F32 = 0, 1
+CP_MASK_NONE, CP_MASK_CAUSAL = 0, 1
+FULL, DIAG, SKIP = 0, 1, 2
+ABI_VERSION = 1
+
+# Every symbol include/ringattn.h declares.
+EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
+            "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
+            "split_kv_decode_workspace", "split_kv_decode")
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, status, func, detail):
+        super().__init__(f"{func}: status {status} ({detail})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ring_attention_02_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_pi64, _pi32 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+
+_lib.cp_abi_version.restype = _i32
+_lib.cp_abi_version.argtypes = []
+_lib.cp_status_string.restype = ctypes.c_char_p
+_lib.cp_status_string.argtypes = [_i32]
+_lib.cp_last_error.restype = ctypes.c_char_p
+_lib.cp_last_error.argtypes = []
+_lib.cp_partition.restype = _i32
+_lib.cp_partition.argtypes = [_vp, _i32, _i32, _i32, _vp, _pi64, _vp, _pi64]
+_lib.cp_slot_mapping.restype = _i32
+_lib.cp_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp]
+_lib.cp_classify.restype = _i32
+_lib.cp_classify.argtypes = [_i64, _i64, _i64, _i64, _i32, _pi32]
+_lib.ring_attn_step.restype = _i32
+_lib.ring_attn_step.argtypes = [_vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
+                                _i64, _i64, _i32, _f32, _i32, _vp, _vp, _pi32, _vp]
+_lib.lse_merge.restype = _i32
+_lib.lse_merge.argtypes = [_vp, _vp, _i32, _i64, _i32, _vp, _i32, _vp, _vp]
+_lib.split_kv_decode_workspace.restype = _sz
+_lib.split_kv_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
+_lib.split_kv_decode.restype = _i32
+_lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i32, _i32, _i32,
+                                 _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+
+if _lib.cp_abi_version() != ABI_VERSION:
+    raise ImportError(f"libringattn ABI {_lib.cp_abi_version()} != binding ABI {ABI_VERSION}")
+
+
+def lib():
+    """The loaded ctypes library (for ABI-level tests)."""
+    return _lib
+
+
+def last_error():
+    return _lib.cp_last_error().decode()
+
+
+def _check(status, func):
+    if status != CP_OK:
+        raise RingAttnError(status, func, last_error() or _lib.cp_status_string(status).decode())
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+# ---------------------------------------------------------------------------
+# host index functions
+# ---------------------------------------------------------------------------
+
+def partition(seq_lens, cp_size, rank):
+    """Head-tail (zigzag) partition: (local token ids of `rank`, restore index)."""
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+    llen, rlen = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.cp_partition(_np_ptr(lens), len(lens), cp_size, rank, None, ctypes.byref(llen),
+                             None, ctypes.byref(rlen)), "cp_partition")
+    local = np.empty(llen.value, dtype=np.int64)
+    restore = np.empty(rlen.value, dtype=np.int64)
+    _check(_lib.cp_partition(_np_ptr(lens), len(lens), cp_size, rank, _np_ptr(local),
+                             ctypes.byref(llen), _np_ptr(restore), ctypes.byref(rlen)),
+           "cp_partition")
+    return local, restore
+
+
+def slot_mapping(positions, block_size, interleave, pcp_size, dcp_size, block_table=None):
+    """Interleaved virtual-block placement: (device int32[n], slot int64[n])."""
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    dev = np.empty(pos.size, dtype=np.int32)
+    slot = np.empty(pos.size, dtype=np.int64)
+    table = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    _check(_lib.cp_slot_mapping(_np_ptr(pos), pos.size, block_size, interleave, pcp_size,
+                                dcp_size, _np_ptr(table), 0 if table is None else table.size,
+                                _np_ptr(dev), _np_ptr(slot)), "cp_slot_mapping")
+    return dev, slot
+
+
+def classify(q_pos0, sq, k_pos0, sk, causal=True):
+    out = ctypes.c_int32(-1)
+    _check(_lib.cp_classify(q_pos0, sq, k_pos0, sk, CP_MASK_CAUSAL if causal else CP_MASK_NONE,
+                            ctypes.byref(out)), "cp_classify")
+    return out.value
+
+
+# ---------------------------------------------------------------------------
+# device functions (torch tensors: memory and streams only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    if t.dtype == torch.float32:
+        return CP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def ring_attn_step(q, k, v, o, lse, q_pos0=0, k_pos0=0, causal=True, scale=None,
+                   accumulate=False, stream=None):
+    """One (Q chunk, KV block) ring step; returns the pair's class (FULL/DIAG/SKIP).
+
+    q [B,Sq,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv] (bf16 or float32);
+    o [B,Sq,Hq,Dv] float32 and lse [B,Sq,Hq] float32 are written (or merged
+    into when accumulate=True).
+    """
+    torch = _torch()
+    B, Sq, Hq, Dqk = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    Dv = v.shape[3]
+    if Bk != B or Dk != Dqk or tuple(v.shape[:3]) != (B, Sk, Hkv):
+        raise ValueError("q/k/v shapes do not agree")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if tuple(o.shape) != (B, Sq, Hq, Dv) or o.dtype != torch.float32:
+        raise ValueError("o must be float32 [B, Sq, Hq, Dv]")
+    if tuple(lse.shape) != (B, Sq, Hq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Sq, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    cls = ctypes.c_int32(-1)
+    _check(_lib.ring_attn_step(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                               _dtype_code(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, int(q_pos0),
+                               int(k_pos0), CP_MASK_CAUSAL if causal else CP_MASK_NONE,
+                               float(scale), 1 if accumulate else 0, _dev_ptr(o, "o"),
+                               _dev_ptr(lse, "lse"), ctypes.byref(cls), _stream_handle(stream)),
+           "ring_attn_step")
+    return cls.value
+
+
+def lse_merge(o_parts, lse_parts, o_out=None, lse_out=None, out_dtype=None, stream=None):
+    """Merge partials o_parts [n, ..., Dv] / lse_parts [n, ...]; returns (o, lse)."""
+    torch = _torch()
+    n = o_parts.shape[0]
+    dv = o_parts.shape[-1]
+    rows_shape = tuple(o_parts.shape[1:-1])
+    if tuple(lse_parts.shape) != (n, *rows_shape):
+        raise ValueError("lse_parts shape does not match o_parts")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    rows = int(np.prod(rows_shape)) if rows_shape else 1
+    out_dtype = out_dtype or torch.float32
+    if o_out is None:
+        o_out = torch.empty((*rows_shape, dv), dtype=out_dtype, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty(rows_shape, dtype=torch.float32, device=o_parts.device)
+    _check(_lib.lse_merge(_dev_ptr(o_parts, "o_parts"), _dev_ptr(lse_parts, "lse_parts"), n, rows,
+                          dv, _dev_ptr(o_out, "o_out"), _dtype_code(o_out),
+                          _dev_ptr(lse_out, "lse_out"), _stream_handle(stream)), "lse_merge")
+    return o_out, lse_out
+
+
+def split_kv_decode_workspace(n_shards, batch, hq, hkv, d_v, t_shard):
+    return int(_lib.split_kv_decode_workspace(n_shards, batch, hq, hkv, d_v, t_shard))
+
+
+def split_kv_decode(q, k_shards, v_shards, shard_lens=None, scale=None, o_parts=None,
+                    lse_parts=None, workspace=None, stream=None):
+    """Per-shard decode partials: q [B,Hq,D], shards [S,B,T,Hkv,D] -> (o_parts, lse_parts)."""
+    torch = _torch()
+    B, Hq, Dqk = q.shape
+    S, Bk, T, Hkv, Dk = k_shards.shape
+    Dv = v_shards.shape[4]
+    if Bk != B or Dk != Dqk or tuple(v_shards.shape[:4]) != (S, B, T, Hkv):
+        raise ValueError("q / shard shapes do not agree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if o_parts is None:
+        o_parts = torch.empty((S, B, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((S, B, Hq), dtype=torch.float32, device=q.device)
+    ws_need = split_kv_decode_workspace(S, B, Hq, Hkv, Dv, T)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    lens_ptr = None
+    if shard_lens is not None:
+        if shard_lens.dtype != torch.int64 or tuple(shard_lens.shape) != (S, B):
+            raise ValueError("shard_lens must be int64 [n_shards, batch]")
+        lens_ptr = _dev_ptr(shard_lens, "shard_lens")
+    _check(_lib.split_kv_decode(_dev_ptr(q, "q"), _dev_ptr(k_shards, "k_shards"),
+                                _dev_ptr(v_shards, "v_shards"), _dtype_code(q), S, B, T, lens_ptr,
+                                Hq, Hkv, Dqk, Dv, float(scale), _dev_ptr(o_parts, "o_parts"),
+                                _dev_ptr(lse_parts, "lse_parts"),
+                                None if workspace is None else _dev_ptr(workspace, "workspace"),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream_handle(stream)), "split_kv_decode")
+    return o_parts, lse_parts
+
+
+from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E402
+
+__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "lse_merge",
+           "split_kv_decode", "split_kv_decode_workspace", "ZigzagRing", "segmented_prefill",
+           "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
+           "last_error"]

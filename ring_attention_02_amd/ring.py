@@ -1,0 +1,175 @@
+"""Ring schedules on one GPU: the zigzag causal ring, segmented prefill and
+the plain (non-causal) ring sweep, all built on the library's calls.
+
+Ring rule (guijiagi.com "Ring Attention", ring-topology excerpt): at step t
+rank i computes with the K/V block that started on rank (i - t) mod N while
+that block travels on to rank i + 1; after N steps its partial output is the
+final result.  With the head-tail partition (vLLM-Ascend "Context Parallel
+(CP)", PCP head-tail token partition paragraph) the block of rank s holds
+sequence parts s and 2N-1-s.
+
+On one GPU the other ranks' K/V live in one full-sequence buffer.  Receiving
+a block is a device-to-device copy on a side stream into one of two staging
+slots, issued one step ahead, so the copy of block t+1 overlaps the
+attention of block t: the double buffering of the video "How Context
+Parallelism Splits Long Sequences Across GPUs" (chapter on the wire budget)
+and of the Excalidraw "Context Parallel (CP) / Ring Attention" diagram
+(rotation overlapped with local attention).  Step 0 uses the rank's own
+block in place.
+"""
+
+import math
+
+from . import ring_attn_step, lse_merge, classify, FULL, DIAG, SKIP
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class ZigzagRing:
+    """One rank's share of a zigzag causal ring prefill, emulated on one GPU.
+
+    k_full / v_full: [1, seq, hkv, d] (bf16 or f32) -- every rank's K/V.
+    The local queries are the rank's two parts, [1, 2*chunk, hq, d_qk].
+    """
+
+    def __init__(self, k_full, v_full, cp_size, rank):
+        torch = _torch()
+        seq = k_full.shape[1]
+        if k_full.shape[0] != 1 or seq % (2 * cp_size) != 0:
+            raise ValueError("k_full must be [1, seq, hkv, d] with seq a multiple of 2*cp_size")
+        self.k_full, self.v_full = k_full, v_full
+        self.cp, self.rank = cp_size, rank
+        self.chunk = seq // (2 * cp_size)
+        c = self.chunk
+        self.q_parts = (rank, 2 * cp_size - 1 - rank)
+        self.steps = [((rank - t) % cp_size, 2 * cp_size - 1 - (rank - t) % cp_size)
+                      for t in range(cp_size)]
+        dev = k_full.device
+        self.kbuf = [torch.empty((2, 1, c, *k_full.shape[2:]), dtype=k_full.dtype, device=dev)
+                     for _ in range(2)]
+        self.vbuf = [torch.empty((2, 1, c, *v_full.shape[2:]), dtype=v_full.dtype, device=dev)
+                     for _ in range(2)]
+        self.side = torch.cuda.Stream(device=dev)          # default priority
+        self.ready = [torch.cuda.Event() for _ in range(2)]
+        self.free = [torch.cuda.Event() for _ in range(2)]
+        self.pending_free = [False, False]
+
+    def local_slices(self, t):
+        return [self.k_full[:, p * self.chunk:(p + 1) * self.chunk] for p in self.steps[t]], \
+               [self.v_full[:, p * self.chunk:(p + 1) * self.chunk] for p in self.steps[t]]
+
+    def _stage(self, t):
+        """Side stream: 'receive' the block of step t into slot t % 2."""
+        torch = _torch()
+        slot = t % 2
+        if self.pending_free[slot]:
+            self.side.wait_event(self.free[slot])
+        ks, vs = self.local_slices(t)
+        with torch.cuda.stream(self.side):
+            for j in range(2):
+                self.kbuf[slot][j].copy_(ks[j], non_blocking=True)
+                self.vbuf[slot][j].copy_(vs[j], non_blocking=True)
+        self.ready[slot].record(self.side)
+
+    def pairs(self):
+        """(step, q part index, kv part index, class) for every pair of the sweep."""
+        c = self.chunk
+        out = []
+        for t, kv_parts in enumerate(self.steps):
+            for qi, qp in enumerate(self.q_parts):
+                for kj, kp in enumerate(kv_parts):
+                    out.append((t, qi, kj, classify(qp * c, c, kp * c, c, True)))
+        return out
+
+    def run(self, q_local, o, lse, scale=None, on_launch=None):
+        """Sweep every ring step; o [1, 2c, hq, dv] / lse [1, 2c, hq] end final.
+
+        on_launch(step, q_index, kv_index, cls, fn) may wrap each launch (the
+        bench uses it to time launches); fn() performs the launch.
+        """
+        torch = _torch()
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)      # inputs written on the main stream are visible
+        c = self.chunk
+        first = [True, True]
+        if self.cp > 1:
+            self._stage(1)
+        for t, kv_parts in enumerate(self.steps):
+            if t == 0:
+                ks, vs = self.local_slices(0)
+            else:
+                main.wait_event(self.ready[t % 2])
+                ks, vs = self.kbuf[t % 2], self.vbuf[t % 2]
+            if 1 <= t and t + 1 < self.cp:
+                self._stage(t + 1)
+            for qi, qp in enumerate(self.q_parts):
+                qs = slice(qi * c, (qi + 1) * c)
+                for kj, kp in enumerate(kv_parts):
+                    acc = not first[qi]
+                    args = (q_local[:, qs], ks[kj], vs[kj], o[:, qs], lse[:, qs])
+                    kw = dict(q_pos0=qp * c, k_pos0=kp * c, causal=True, scale=scale,
+                              accumulate=acc)
+                    if on_launch is None:
+                        ring_attn_step(*args, **kw)
+                    else:
+                        cls = classify(qp * c, c, kp * c, c, True)
+                        on_launch(t, qi, kj, cls, lambda a=args, k=kw: ring_attn_step(*a, **k))
+                    first[qi] = False
+            if t >= 1:
+                self.free[t % 2].record(main)
+                self.pending_free[t % 2] = True
+        # the staging buffers are reused by the next sweep only after this one
+        main.wait_stream(self.side)
+        return o, lse
+
+
+def segmented_prefill(q, k, v, o, lse, q_pos0, segment, k_pos0=0, causal=True, scale=None,
+                      on_launch=None):
+    """Attend q to k/v one KV segment at a time with an online-softmax merge.
+
+    vLLM-Ascend "Context Parallel (CP)", PCP chunked-prefill paragraph: with a
+    cap on the KV processed per round, the segments are attended in order and
+    each result is folded into the running one.  q [1, Sq, H, Dqk] at
+    positions q_pos0.., k/v [1, Sk, Hkv, *] at positions k_pos0.. (read in
+    place); o/lse are overwritten with the result.
+    """
+    sk = k.shape[1]
+    n_seg = max(1, math.ceil(sk / segment))
+    for s in range(n_seg):
+        a, b = s * segment, min(sk, (s + 1) * segment)
+        args = (q, k[:, a:b], v[:, a:b], o, lse)
+        kw = dict(q_pos0=q_pos0, k_pos0=k_pos0 + a, causal=causal, scale=scale, accumulate=s > 0)
+        if on_launch is None:
+            ring_attn_step(*args, **kw)
+        else:
+            cls = classify(q_pos0, q.shape[1], k_pos0 + a, b - a, causal)
+            on_launch(s, 0, s, cls, lambda a_=args, k_=kw: ring_attn_step(*a_, **k_))
+    return o, lse
+
+
+def noncausal_ring_sweep(q, k, v, n_blocks, scale=None):
+    """Plain ring over n_blocks sequence blocks, no mask, fresh partial per step.
+
+    Block qb meets K/V block (qb - t) mod n at step t; the n partials of every
+    query row are combined with lse_merge.  Returns (o, lse) for all rows.
+    """
+    torch = _torch()
+    B, S, H, D = q.shape
+    dv = v.shape[3]
+    blk = S // n_blocks
+    if blk * n_blocks != S:
+        raise ValueError("sequence must split into n_blocks equal blocks")
+    o_parts = torch.empty((n_blocks, B, S, H, dv), dtype=torch.float32, device=q.device)
+    lse_parts = torch.empty((n_blocks, B, S, H), dtype=torch.float32, device=q.device)
+    for qb in range(n_blocks):
+        qs = slice(qb * blk, (qb + 1) * blk)
+        for t in range(n_blocks):
+            kb = (qb - t) % n_blocks
+            ks = slice(kb * blk, (kb + 1) * blk)
+            ring_attn_step(q[:, qs], k[:, ks].contiguous(), v[:, ks].contiguous(),
+                           o_parts[t][:, qs], lse_parts[t][:, qs], q_pos0=qb * blk,
+                           k_pos0=kb * blk, causal=False, scale=scale, accumulate=False)
+    return lse_merge(o_parts, lse_parts)

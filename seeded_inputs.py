@@ -62,3 +62,24 @@ CONFIGS = {
     5: dict(name="segmented chunked prefill, MLA shape", q_len=4096, q_pos0=131072,
             heads=128, d_qk=192, d_v=128, kv_len=135168, segment=8192, dtype="bf16"),
 }
+
+
+def device_seed(cfg, tensor_id, chunk_id=0):
+    """63-bit seed for a device-side generator, from the same SeedSequence key."""
+    state = np.random.SeedSequence((cfg, tensor_id, chunk_id)).generate_state(1, dtype=np.uint64)
+    return int(state[0] & np.uint64((1 << 63) - 1))
+
+
+def device_normal(cfg, tensor_id, chunk_id, shape, dtype, device):
+    """N(0, 1) draws made on the GPU (for inputs too large to draw on the host).
+
+    torch's device generator is seeded from (cfg, tensor, chunk); float32 draws
+    are rounded to `dtype` (round-to-nearest-even for bf16).  The oracle reads
+    back exactly the values the kernels receive, so both sides see the same
+    inputs.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(cfg, tensor_id, chunk_id))
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+    return x if dtype == torch.float32 else x.to(dtype)

@@ -1,0 +1,228 @@
+"""GPU parity of every entry point against the CPU oracle, element by element,
+on seeded inputs small enough for the oracle (several tiles plus ragged
+tails), with the edge cases of the method: empty rows, SKIP pairs, single
+keys, GQA groups, every supported head-dim pair, accumulate on and off."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import tensor, host64, compare, say, F32_O, BF16_O, BF16_LSE
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import ring_attention_02_amd as ra
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return ra
+
+
+CASES = [
+    # (B, sq, sk, hq, hkv, dqk, dv, q_pos0, k_pos0, causal)
+    (1, 128, 64, 2, 2, 128, 128, 0, 0, False),
+    (1, 200, 333, 4, 2, 128, 128, 0, 0, False),          # ragged tails, GQA 2
+    (2, 130, 70, 8, 1, 64, 64, 0, 0, False),             # GQA 8, batch 2
+    (1, 257, 257, 4, 4, 128, 128, 0, 0, True),           # self-causal diagonal, ragged
+    (1, 300, 200, 2, 1, 192, 128, 500, 250, True),       # MLA shape, diagonal offset
+    (1, 100, 64, 2, 2, 128, 128, 100, 150, True),        # rows 100..149 see nothing
+    (1, 1, 1, 1, 1, 64, 64, 0, 0, True),                 # one query, one key
+    (1, 1, 500, 16, 2, 128, 128, 1000, 0, True),         # one query sees all (FULL)
+    (1, 64, 1024, 4, 1, 64, 64, 2000, 1500, True),       # partial diagonal, many tiles
+    (1, 384, 128, 16, 16, 192, 128, 128, 0, True),       # FULL (every pair visible)
+]
+
+
+def _run_case(ra, idx, case, dtype, accumulate):
+    B, sq, sk, hq, hkv, dqk, dv, q0, k0, causal = case
+    say(f"case {idx}: B={B} sq={sq} sk={sk} hq={hq} hkv={hkv} d=({dqk},{dv}) q0={q0} k0={k0} "
+        f"causal={causal} dtype={dtype} acc={accumulate}")
+    cfg = 100 + idx
+    q, q64 = tensor(cfg, 1, 0, (B, sq, hq, dqk), dtype)
+    k, k64 = tensor(cfg, 2, 0, (B, sk, hkv, dqk), dtype)
+    v, v64 = tensor(cfg, 3, 0, (B, sk, hkv, dv), dtype)
+    scale = 1.0 / np.sqrt(dqk)
+    q_pos, k_pos = q0 + np.arange(sq), k0 + np.arange(sk)
+    o = torch.full((B, sq, hq, dv), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((B, sq, hq), 7.0, dtype=torch.float32, device="cuda")
+    if accumulate:
+        # a previous ring step against another K/V block sitting just before this one
+        sk2 = 96
+        k2, k2_64 = tensor(cfg, 4, 0, (B, sk2, hkv, dqk), dtype)
+        v2, v2_64 = tensor(cfg, 5, 0, (B, sk2, hkv, dv), dtype)
+        ra.ring_attn_step(q, k2, v2, o, lse, q0, k0 - sk2, causal, scale, accumulate=False)
+        cls = ra.ring_attn_step(q, k, v, o, lse, q0, k0, causal, scale, accumulate=True)
+        o_ref, lse_ref = oracle.attention_ref(
+            q64, np.concatenate([k2_64, k64], 1), np.concatenate([v2_64, v64], 1), q_pos,
+            np.concatenate([k0 - sk2 + np.arange(sk2), k_pos]), causal, scale)
+    else:
+        cls = ra.ring_attn_step(q, k, v, o, lse, q0, k0, causal, scale, accumulate=False)
+        o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, q_pos, k_pos, causal, scale)
+    torch.cuda.synchronize()
+    assert cls == oracle.classify_ref(q0, sq, k0, sk, causal)
+    tol_o = F32_O if dtype == torch.float32 else BF16_O
+    tol_l = F32_O if dtype == torch.float32 else BF16_LSE
+    compare(host64(o), host64(lse), o_ref, lse_ref, tol_o, tol_l, f"case {idx}")
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)))
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_ring_attn_step_bf16(ra, idx, accumulate):
+    _run_case(ra, idx, CASES[idx], torch.bfloat16, accumulate)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_ring_attn_step_f32(ra, idx, accumulate):
+    _run_case(ra, idx, CASES[idx], torch.float32, accumulate)
+
+
+def test_skip_pair_writes_identity_or_nothing(ra):
+    q, _ = tensor(7, 1, 0, (1, 64, 2, 128), torch.bfloat16)
+    k, _ = tensor(7, 2, 0, (1, 64, 2, 128), torch.bfloat16)
+    v, _ = tensor(7, 3, 0, (1, 64, 2, 128), torch.bfloat16)
+    o = torch.full((1, 64, 2, 128), 3.0, device="cuda")
+    lse = torch.full((1, 64, 2), 5.0, device="cuda")
+    cls = ra.ring_attn_step(q, k, v, o, lse, q_pos0=0, k_pos0=64, causal=True, accumulate=True)
+    torch.cuda.synchronize()
+    assert cls == ra.SKIP
+    assert torch.all(o == 3.0) and torch.all(lse == 5.0)
+    cls = ra.ring_attn_step(q, k, v, o, lse, q_pos0=0, k_pos0=64, causal=True, accumulate=False)
+    torch.cuda.synchronize()
+    assert cls == ra.SKIP
+    assert torch.all(o == 0.0) and torch.all(torch.isneginf(lse))
+
+
+def test_deterministic(ra):
+    q, _ = tensor(8, 1, 0, (1, 300, 4, 128), torch.bfloat16)
+    k, _ = tensor(8, 2, 0, (1, 500, 2, 128), torch.bfloat16)
+    v, _ = tensor(8, 3, 0, (1, 500, 2, 128), torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((1, 300, 4, 128), device="cuda")
+        lse = torch.empty((1, 300, 4), device="cuda")
+        ra.ring_attn_step(q, k, v, o, lse, q_pos0=400, k_pos0=0, causal=True)
+        outs.append((o.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("n,rows,dv,out_bf16", [(1, 37, 64, False), (4, 512, 64, False),
+                                                (8, 4096, 128, False), (3, 1000, 128, True),
+                                                (2, 65, 192, False)])
+def test_lse_merge(ra, n, rows, dv, out_bf16):
+    say(f"lse_merge n={n} rows={rows} dv={dv} bf16={out_bf16}")
+    r = np.random.default_rng(n * 1000 + rows)
+    o_parts = r.standard_normal((n, rows, dv)).astype(np.float32)
+    lse_parts = (r.standard_normal((n, rows)) * 3).astype(np.float32)
+    lse_parts[:, :5] = -np.inf                  # rows with nothing anywhere
+    o_parts[:, :5] = 0.0
+    if n > 1:
+        lse_parts[0, 5:20] = -np.inf            # one empty part
+        o_parts[0, 5:20] = 0.0
+    o_ref, lse_ref = oracle.lse_merge_ref(list(o_parts.astype(np.float64)),
+                                          list(lse_parts.astype(np.float64)))
+    od, ld = ra.lse_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda(),
+                          out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    compare(host64(od), host64(ld), o_ref, lse_ref, 1e-2 if out_bf16 else 1e-5, 1e-5, "lse_merge")
+
+
+def test_zigzag_all_ranks_restore(ra):
+    """Every rank of a small zigzag ring; gathered outputs put back in order
+    with the restore index equal full causal attention."""
+    seq, cp, h, d = 2048, 4, 4, 128
+    k, k64 = tensor(21, 2, 0, (1, seq, h, d), torch.bfloat16)
+    v, v64 = tensor(21, 3, 0, (1, seq, h, d), torch.bfloat16)
+    q_all, q64 = tensor(21, 1, 0, (1, seq, h, d), torch.bfloat16)
+    gathered_o, gathered_l = [], []
+    restore = None
+    for rank in range(cp):
+        local, restore = ra.partition([seq], cp, rank)
+        idx = torch.from_numpy(local).cuda()
+        q_local = q_all.index_select(1, idx).contiguous()
+        ring = ra.ZigzagRing(k, v, cp, rank)
+        o = torch.empty((1, len(local), h, d), device="cuda")
+        lse = torch.empty((1, len(local), h), device="cuda")
+        ring.run(q_local, o, lse)
+        gathered_o.append(o)
+        gathered_l.append(lse)
+    o = torch.cat(gathered_o, 1)[:, torch.from_numpy(restore).cuda()]
+    lse = torch.cat(gathered_l, 1)[:, torch.from_numpy(restore).cuda()]
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, causal=True)
+    compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "zigzag all ranks")
+
+
+def test_noncausal_ring_sweep_f32(ra):
+    q, q64 = tensor(1, 1, 0, (1, 512, 4, 64), torch.float32)
+    k, k64 = tensor(1, 2, 0, (1, 512, 4, 64), torch.float32)
+    v, v64 = tensor(1, 3, 0, (1, 512, 4, 64), torch.float32)
+    o, lse = ra.noncausal_ring_sweep(q, k, v, 4)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, causal=False)
+    compare(host64(o), host64(lse), o_ref, lse_ref, F32_O, F32_O, "tiny ring fp32")
+
+
+def test_segmented_prefill_small(ra):
+    sq, h, dqk, dv, q0 = 256, 4, 192, 128, 1000
+    skv = q0 + sq
+    q, q64 = tensor(31, 1, 0, (1, sq, h, dqk), torch.bfloat16)
+    k, k64 = tensor(31, 2, 0, (1, skv, h, dqk), torch.bfloat16)
+    v, v64 = tensor(31, 3, 0, (1, skv, h, dv), torch.bfloat16)
+    o = torch.empty((1, sq, h, dv), device="cuda")
+    lse = torch.empty((1, sq, h), device="cuda")
+    ra.segmented_prefill(q, k, v, o, lse, q_pos0=q0, segment=300)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, q0 + np.arange(sq), np.arange(skv), True)
+    compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "segmented")
+
+
+def _decode_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs=128, il=16):
+    d = 128
+    tmax = max(ctx_lens)
+    vbs = bs * n_shards
+    t_shard = -(-tmax // vbs) * bs
+    q, q64 = tensor(cfg, 1, 0, (B, hq, d), torch.bfloat16)
+    k_ctx, k64 = tensor(cfg, 2, 0, (B, tmax, hkv, d), torch.bfloat16)
+    v_ctx, v64 = tensor(cfg, 3, 0, (B, tmax, hkv, d), torch.bfloat16)
+    ks = torch.zeros((n_shards, B, t_shard, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vs = torch.zeros_like(ks)
+    lens = np.zeros((n_shards, B), dtype=np.int64)
+    for b, L in enumerate(ctx_lens):
+        dev, slot = ra.slot_mapping(np.arange(L), bs, il, n_shards, 1)
+        lens[:, b] = np.bincount(dev, minlength=n_shards)
+        dev_t = torch.from_numpy(dev.astype(np.int64)).cuda()
+        slot_t = torch.from_numpy(slot).cuda()
+        ks[dev_t, b, slot_t] = k_ctx[b, :L]
+        vs[dev_t, b, slot_t] = v_ctx[b, :L]
+    lens_t = torch.from_numpy(lens).cuda()
+    o_parts, lse_parts = ra.split_kv_decode(q, ks, vs, shard_lens=lens_t)
+    o, lse = ra.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    for b, L in enumerate(ctx_lens):
+        dev_ref, _ = oracle.slot_mapping_ref(np.arange(L), bs, il, n_shards, 1)
+        po, pl, mo, ml = oracle.decode_shards_ref(q64[b:b + 1], k64[b:b + 1, :L], v64[b:b + 1, :L],
+                                                  dev_ref, n_shards)
+        compare(host64(o_parts[:, b]), host64(lse_parts[:, b]), po[:, 0], pl[:, 0], BF16_O,
+                BF16_LSE, f"decode partials b={b}")
+        compare(host64(o[b]), host64(lse[b]), mo[0], ml[0], BF16_O, BF16_LSE, f"decode b={b}")
+
+
+def test_split_kv_decode_small(ra):
+    say("decode: 8 shards, 3 requests (one ragged), GQA 8")
+    _decode_case(ra, 41, 3, [4096, 1500, 4096], 8, 16, 2)
+
+
+def test_split_kv_decode_with_splits(ra):
+    # few work items -> the kernel splits each shard's keys and merges the splits
+    assert ra.split_kv_decode_workspace(2, 1, 4, 1, 128, 8192) > 0
+    say("decode: 2 shards, 1 request, splits")
+    _decode_case(ra, 42, 1, [16384 - 100], 2, 4, 1)
+
+
+def test_split_kv_decode_group16_and_empty_shard(ra):
+    say("decode: group 16, shard with no tokens")
+    _decode_case(ra, 43, 2, [100, 2048], 8, 16, 1)
