@@ -1,0 +1,334 @@
+"""Benchmark of the blockwise ring-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--primary-only]
+                    [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline workload is the zigzag causal ring
+prefill of one rank: seq 8192, cp 4 (8 chunks of 1024), rank 0 holding Q
+chunks {0, 7}, 32 heads, d 128, bf16 with float32 accumulation.  A step is
+one full ring sweep of that rank: 4 ring steps, each staging the next K/V
+block on a side stream while the 4 (Q chunk, K/V chunk) pairs of the current
+block run (7 FULL, 2 DIAG and 7 SKIP pairs overall), merged in place.
+`value` is algorithmic causal-attention TFLOP/s: visible (q, k) pairs x
+heads x (2 d_qk + 2 d_v) per sweep / time per sweep.
+
+Also reported in the same line (unless --primary-only): the long zigzag
+prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
+(GB/s against HBM), segmented chunked prefill (MLA shape) and a standalone
+LSE merge, each with the roofline of its dominant kernel, plus the CPU
+oracle timed on the host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "causal attn TFLOP/s per ring-step prefill + decode GB/s, % of roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--primary-only", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of secondary workloads to run")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_launch_stats(launch_list, reps):
+    """Average duration (ms) of the attention kernel launches of one step.
+
+    The step's kernel launches (no copies) are captured back to back in a HIP
+    graph and replayed `reps` times between two HIP events on the replay
+    stream, so the figure is kernel time plus the dispatch gaps between
+    consecutive kernels -- no host overhead, no event per launch.
+    """
+    import torch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for fn in launch_list:          # warm: first launch outside the graph
+            fn()
+        with torch.cuda.graph(graph, stream=stream):
+            for fn in launch_list:
+                fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        s.record()
+        for _ in range(reps):
+            graph.replay()
+        e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (reps * len(launch_list))
+
+
+def zigzag_launches(w, cls_filter=None):
+    """The non-SKIP ring_attn_step launches of one zigzag sweep (K/V read in place)."""
+    import ring_attention_02_amd as ra
+    ring, q, o, lse, c = w["ring"], w["q_local"], w["o"], w["lse"], w["chunk"]
+    out = []
+    first = [True, True]
+    for t, kv_parts in enumerate(ring.steps):
+        ks, vs = ring.local_slices(t)
+        for qi, qp in enumerate(ring.q_parts):
+            qs = slice(qi * c, (qi + 1) * c)
+            for kj, kp in enumerate(kv_parts):
+                cls = ra.classify(qp * c, c, kp * c, c, True)
+                acc = not first[qi]
+                first[qi] = False
+                if cls == ra.SKIP and acc:
+                    continue
+                if cls_filter is not None and cls != cls_filter:
+                    continue
+                out.append(lambda a=(q[:, qs], ks[kj], vs[kj], o[:, qs], lse[:, qs]),
+                           k=dict(q_pos0=qp * c, k_pos0=kp * c, causal=True, accumulate=acc):
+                           ra.ring_attn_step(*a, **k))
+    return out
+
+
+def time_steps(step_fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step_fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step_fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def roofline_entry(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.zigzag_setup(cfg_id)
+    ring, q, o, lse = w["ring"], w["q_local"], w["o"], w["lse"]
+    eager = time_steps(lambda: ring.run(q, o, lse), steps, warmup)
+    sec = eager
+    if use_graph:
+        graph = ring.capture(q, o, lse)
+        sec = time_steps(graph.replay, steps, warmup)
+    launches = zigzag_launches(w)
+    reps = max(2, min(steps, 20)) if cfg_id == 2 else 1
+    mean_ms = kernel_launch_stats(launches, reps)
+    flops_per_launch = w["flops"] / len(launches)
+    achieved = flops_per_launch / (mean_ms * 1e-3) / 1e12
+    full_ms = kernel_launch_stats(zigzag_launches(w, ra.FULL), reps)
+    diag_ms = kernel_launch_stats(zigzag_launches(w, ra.DIAG), reps)
+    return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=len(launches),
+                        flops_per_launch=flops_per_launch, achieved_tflops=achieved,
+                        full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3)
+
+
+def decode_bench(steps, warmup):
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.decode_setup()
+    o_parts = torch.empty((w["n_shards"], w["B"], w["hq"], w["d"]), device="cuda")
+    lse_parts = torch.empty((w["n_shards"], w["B"], w["hq"]), device="cuda")
+    o = torch.empty((w["B"], w["hq"], w["d"]), device="cuda")
+    lse = torch.empty((w["B"], w["hq"]), device="cuda")
+
+    def step():
+        ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
+                           lse_parts=lse_parts)
+        ra.lse_merge(o_parts, lse_parts, o_out=o, lse_out=lse)
+
+    sec = time_steps(step, steps, warmup)
+    # the decode kernel alone, HIP events on its stream
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    durs = []
+    for _ in range(max(3, min(steps, 10))):
+        s.record()
+        ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
+                           lse_parts=lse_parts)
+        e.record()
+        torch.cuda.synchronize()
+        durs.append(s.elapsed_time(e))
+    kern_ms = float(np.mean(durs))
+    kern_bytes = w["kv_bytes"] + w["q"].numel() * 2 + w["n_shards"] * w["B"] * w["hq"] * (w["d"] + 1) * 4
+    return w, sec, dict(kernel_ms=kern_ms, kernel_bytes=kern_bytes,
+                        kernel_gbs=kern_bytes / (kern_ms * 1e-3) / 1e9)
+
+
+def segmented_bench(steps, warmup):
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.segmented_setup()
+    launches = []
+
+    def collect(step, qi, kj, cls, fn):
+        launches.append(fn)
+
+    def run(cb=None):
+        ra.segmented_prefill(w["q"], w["k"], w["v"], w["o"], w["lse"], q_pos0=w["q_pos0"],
+                             segment=w["segment"], on_launch=cb)
+
+    sec = time_steps(run, steps, warmup)
+    run(collect)
+    mean_ms = kernel_launch_stats(launches, 1)
+    achieved = w["flops"] / len(launches) / (mean_ms * 1e-3) / 1e12
+    return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=len(launches),
+                        achieved_tflops=achieved)
+
+
+def merge_bench(steps, warmup):
+    import torch
+    import ring_attention_02_amd as ra
+    rows, dv, n = 131072 * 64, 128, 2       # the long prefill's rows, two partials
+    o_parts = torch.randn((n, rows, dv), device="cuda")
+    lse_parts = torch.randn((n, rows), device="cuda")
+    o = torch.empty((rows, dv), device="cuda")
+    lse = torch.empty((rows,), device="cuda")
+    sec = time_steps(lambda: ra.lse_merge(o_parts, lse_parts, o_out=o, lse_out=lse), steps, warmup)
+    nbytes = (n * rows * (dv + 1) + rows * (dv + 1)) * 4
+    return sec, nbytes
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host, on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w):
+    import oracle
+    import workloads
+    k = w["k_full"][0].float().cpu().numpy().astype(np.float64)
+    v = w["v_full"][0].float().cpu().numpy().astype(np.float64)
+    q = w["q_local"][0].float().cpu().numpy().astype(np.float64)
+    q_pos = np.asarray(w["local"], dtype=np.int64)
+    heads_done, pairs_done, t_used = 0, 0, 0.0
+    budget = 15.0
+    for h in range(w["hq"]):
+        t0 = time.perf_counter()
+        oracle.attention_ref(q[None, :, h:h + 1], k[None, :, h:h + 1], v[None, :, h:h + 1],
+                             q_pos, np.arange(k.shape[0]), causal=True)
+        t_used += time.perf_counter() - t0
+        heads_done += 1
+        if t_used > budget:
+            break
+    flops = w["pairs"] * heads_done * (2 * w["d"] + 2 * w["d"])
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"rank-0 local queries (2048 tokens) x all 8192 keys for {heads_done} of "
+                      f"{w['hq']} heads, float64 numpy, {t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is one "
+              f"GPU's share of the ring and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import ring_attention_02_amd  # noqa: F401  (fails loudly if the library is missing)
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+
+    log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
+    w2, sec2, l2 = zigzag_bench(2, args.steps, args.warmup)
+    value = w2["flops"] / sec2 / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec2 * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "zigzag causal ring prefill, one rank's share: seq 8192, cp 4 "
+                               "(8 chunks of 1024), rank 0 holds Q chunks {0,7}, 32 heads, "
+                               "d 128, bf16",
+                   "global_batch": 1, "seq_len": 8192, "parallelism": "cp4 ring emulated on 1 GPU",
+                   "flops_per_step": w2["flops"]},
+        "roofline": roofline_entry("mfma", l2["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "kernel": {"name": "attn_step_bf16_kernel<128,128>",
+                   "mean_launch_ms": round(l2["mean_launch_ms"], 5),
+                   "launches_per_step": l2["launches_per_step"],
+                   "full_pair_ms": round(l2["full_ms"], 5), "diag_pair_ms": round(l2["diag_ms"], 5),
+                   "timing": "HIP-graph replay of the step's kernels back to back, HIP events"},
+        "launch": {"mode": "HIP graph replay of the whole sweep (copies + kernels)",
+                   "eager_ms_per_step": round(l2["eager_ms"], 4)},
+    }
+    del w2["ring"]
+    if not args.no_cpu_baseline:
+        log("CPU baseline (oracle on host)")
+        out["cpu_baseline"] = cpu_baseline(w2)
+    del w2
+    torch.cuda.empty_cache()
+
+    if not args.primary_only:
+        only = set(filter(None, args.only.split(",")))
+        sec = {}
+        if not only or "c4" in only:
+            log("C4: zigzag causal prefill, 1M tokens, cp 8, rank 0")
+            w4, s4, l4 = zigzag_bench(4, max(1, min(args.steps, 2)), 1, use_graph=False)
+            sec["long_prefill_1M_cp8"] = {
+                "value": round(w4["flops"] / s4 / 1e12, 3), "unit": "TFLOP/s",
+                "ms_per_step": round(s4 * 1e3, 3), "flops_per_step": w4["flops"],
+                "roofline": roofline_entry("mfma", l4["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+                "full_pair_ms": round(l4["full_ms"], 3), "diag_pair_ms": round(l4["diag_ms"], 3)}
+            del w4
+            torch.cuda.empty_cache()
+        if not only or "c3" in only:
+            log("C3: GQA decode, 64 x 131072 context, 8 shards")
+            w3, s3, l3 = decode_bench(max(3, min(args.steps, 10)), 2)
+            sec["decode_gqa_8_shards"] = {
+                "value": round(w3["bytes"] / s3 / 1e9, 1), "unit": "GB/s",
+                "ms_per_step": round(s3 * 1e3, 4), "bytes_per_step": w3["bytes"],
+                "roofline": roofline_entry("hbm", l3["kernel_gbs"], PEAK_HBM_GBS, "GB/s"),
+                "kernel_ms": round(l3["kernel_ms"], 4)}
+            del w3
+            torch.cuda.empty_cache()
+        if not only or "c5" in only:
+            log("C5: segmented chunked prefill, MLA shape")
+            w5, s5, l5 = segmented_bench(max(2, min(args.steps, 5)), 1)
+            sec["segmented_prefill_mla"] = {
+                "value": round(w5["flops"] / s5 / 1e12, 3), "unit": "TFLOP/s",
+                "ms_per_step": round(s5 * 1e3, 3), "flops_per_step": w5["flops"],
+                "roofline": roofline_entry("mfma", l5["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+                "mean_launch_ms": round(l5["mean_launch_ms"], 4)}
+            del w5
+            torch.cuda.empty_cache()
+        if not only or "merge" in only:
+            log("lse_merge: 2 partials x 8.4M rows x 128")
+            s6, b6 = merge_bench(max(5, args.steps), 2)
+            sec["lse_merge_2x8M"] = {
+                "value": round(b6 / s6 / 1e9, 1), "unit": "GB/s", "ms_per_step": round(s6 * 1e3, 4),
+                "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s")}
+        out["secondary"] = sec
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,6 +125,28 @@ class ZigzagRing:
         main.wait_stream(self.side)
         return o, lse
 
+    def capture(self, q_local, o, lse, scale=None):
+        """Record one whole sweep (copies, events and kernels) as a HIP graph.
+
+        Replaying the graph runs the same launches as run() without the
+        host-side cost of issuing them one by one; the buffers passed here
+        are the ones every replay reads and writes.
+        """
+        torch = _torch()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()                      # default priority
+        stream.wait_stream(torch.cuda.current_stream())
+        saved = list(self.pending_free)
+        self.pending_free = [False, False]               # no cross-replay waits inside the graph
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                self.run(q_local, o, lse, scale=scale)
+        torch.cuda.current_stream().wait_stream(stream)
+        self.pending_free = saved
+        torch.cuda.synchronize()
+        return graph
+
 
 def segmented_prefill(q, k, v, o, lse, q_pos0, segment, k_pos0=0, causal=True, scale=None,
                       on_launch=None):

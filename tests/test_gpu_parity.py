@@ -226,3 +226,31 @@ def test_split_kv_decode_with_splits(ra):
 def test_split_kv_decode_group16_and_empty_shard(ra):
     say("decode: group 16, shard with no tokens")
     _decode_case(ra, 43, 2, [100, 2048], 8, 16, 1)
+
+
+def test_zigzag_graph_replay_matches_eager(ra):
+    """The captured sweep, replayed several times with eager work and
+    synchronisations in between, reproduces the eager sweep bit for bit."""
+    seq, cp, rank, h, d = 2048, 4, 1, 4, 128
+    k, _ = tensor(22, 2, 0, (1, seq, h, d), torch.bfloat16)
+    v, _ = tensor(22, 3, 0, (1, seq, h, d), torch.bfloat16)
+    q_all, _ = tensor(22, 1, 0, (1, seq, h, d), torch.bfloat16)
+    local, _ = ra.partition([seq], cp, rank)
+    q_local = q_all.index_select(1, torch.from_numpy(local).cuda()).contiguous()
+    ring = ra.ZigzagRing(k, v, cp, rank)
+    o = torch.empty((1, len(local), h, d), device="cuda")
+    lse = torch.empty((1, len(local), h), device="cuda")
+    ring.run(q_local, o, lse)
+    torch.cuda.synchronize()
+    o_eager, lse_eager = o.clone(), lse.clone()
+    graph = ring.capture(q_local, o, lse)
+    for i in range(3):
+        o.fill_(float(i + 1))
+        lse.fill_(-float(i + 1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager) and torch.equal(lse, lse_eager), f"replay {i}"
+        ring.run(q_local, o, lse)        # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager)
