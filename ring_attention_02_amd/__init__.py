@@ -4,7 +4,7 @@ Every function here only marshals arguments for the C ABI declared in
 ``include/ringattn.h``; all the work runs in the library (host index code in
 C++, attention / merge / decode in HIP kernels for gfx950).  PyTorch is used
 for device memory and streams only.  Importing this package fails loudly
-when the library has not been built (``python -m ring_attention_02_amd.build``):
+when the library has not been built (``python ring_attention_02_amd/build.py``):
 there is no fallback implementation.
 """
 
@@ -36,7 +36,7 @@ class RingAttnError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ring_attention_02_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python ring_attention_02_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t

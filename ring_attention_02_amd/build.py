@@ -1,6 +1,6 @@
 """Builds libringattn.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m ring_attention_02_amd.build
+    python ring_attention_02_amd/build.py
 
 Sources compile in parallel into ``_build/`` next to this file and link into
 ``libringattn.so`` in the package directory, where the binding loads it.

@@ -71,33 +71,53 @@ __device__ __forceinline__ float merge_weights(float lse_old, float lse_blk, flo
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-constexpr int kBM = 128;  // query rows per workgroup
+constexpr int kBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kThreads = 256;
+constexpr float kTau = 8.f;  // log2 headroom before the running max must be raised
 
 template <int DQK, int DV>
 struct Bf16Cfg {
-  static constexpr int KPITCH = DQK + 8;   // bf16 elements per K row in LDS (+16 B)
-  static constexpr int VPITCH = DV + 32;   // bf16 elements per V row in LDS (+64 B)
-  static constexpr int KCH = kBN * DQK / 8 / kThreads;  // 16-B chunks per thread, K tile
-  static constexpr int VCH = kBN * DV / 8 / kThreads;   // 16-B chunks per thread, V tile
-  static constexpr int QC = DQK / 16;  // 16-wide d chunks (MFMA K steps) for Q K^T
-  static constexpr int DB = DV / 32;   // 32-wide d_v blocks of O^T
-  static_assert(KCH * kThreads * 8 == kBN * DQK, "K tile must split evenly");
-  static_assert(VCH * kThreads * 8 == kBN * DV, "V tile must split evenly");
+  static constexpr int KCPR = DQK / 8;               // 16-byte chunks per K row
+  static constexpr int VCPR = DV / 8;                // 16-byte chunks per V row
+  static constexpr int KTILE = kBN * DQK;            // bf16 elements of one K stage
+  static constexpr int VTILE = kBN * DV;             // bf16 elements of one V stage
+  static constexpr int KDMA = kBN * KCPR / kThreads;  // 16-B direct loads per thread per K tile
+  static constexpr int VDMA = kBN * VCPR / kThreads;
+  static constexpr int QC = DQK / 16;  // MFMA steps of S^T = K Q^T
+  static constexpr int DB = DV / 32;   // 32-row d_v blocks of O^T
+  static_assert(KDMA * kThreads == kBN * KCPR && VDMA * kThreads == kBN * VCPR, "tile split");
 };
+
+// XOR swizzles of the 16-byte chunks inside a K / V row of LDS (self-inverse).
+// K: the 16 lanes of a read quarter hold 16 consecutive keys and one chunk
+// index; the swizzle spreads them over all 64 banks.
+template <int CPR>
+__device__ __forceinline__ int kswz(int c, int r) {
+  if constexpr (CPR == 16) return c ^ (r & 15);
+  else return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7));   // rows of 128 or 384 bytes
+}
+// V: a transposed read takes 4 consecutive rows x 2 (per 16 lanes) or x 4
+// (per 32 lanes) chunks; the swizzle puts those on distinct banks.
+template <int CPR>
+__device__ __forceinline__ int vswz(int c, int r) {
+  if constexpr (CPR == 16) return c ^ (4 * (r & 3));
+  else return c ^ (4 * ((r >> 1) & 1));                // rows of 128 bytes
+}
 
 template <int DQK, int DV>
 __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a) {
   using C = Bf16Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * C::KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * C::VPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * C::VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query row within the wave (B / C column)
-  const int hh = lane >> 5;   // which half of the contraction slice this lane holds
+  const int hh = lane >> 5;   // which half of each contraction slice this lane holds
+  const int g = lane >> 4;    // 16-lane group (transposed V reads)
+  const int i16 = lane & 15;
 
   const int logical = xcd_contiguous_id(blockIdx.x, a.total_wgs);
   int qt = logical % a.n_qtiles;
@@ -114,11 +134,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
   const int64_t q_first = static_cast<int64_t>(qt) * kBM;
   const int64_t q_last = min(a.sq, q_first + kBM) - 1;  // last valid local row of the WG
   const int64_t wq0 = q_first + wave * 32;              // first row of this wave
-  const int64_t wq_last = min(wq0 + 31, a.sq - 1);
   const int64_t my_row = wq0 + col;
   const bool row_valid = my_row < a.sq;
+  const int64_t qpos = a.q_pos0 + my_row;
 
-  // Number of keys any row of this workgroup can see.
+  // Keys any row of this workgroup can see.
   int64_t nkeys = a.sk;
   if (a.causal) {
     const int64_t lim = a.q_pos0 + q_last - a.k_pos0 + 1;
@@ -126,14 +146,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
   }
   const int ntiles = static_cast<int>((nkeys + kBN - 1) / kBN);
 
-  // Q fragment: for chunk c, lane holds Q[row][16c + 8hh .. +7] (B operand).
+  // Q^T fragment (B operand): for step c the lane holds Q[row][16c + 8hh .. +7].
   bf16x8 qf[C::QC];
   {
-    const uint16_t* qp = qg + ((static_cast<int64_t>(b) * a.sq + my_row) * a.hq + h) * DQK;
+    const uint16_t* qp = qg + ((static_cast<int64_t>(b) * a.sq + (row_valid ? my_row : 0)) * a.hq + h) * DQK;
 #pragma unroll
     for (int c = 0; c < C::QC; ++c) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (row_valid) raw = *reinterpret_cast<const u32x4*>(qp + 16 * c + 8 * hh);
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * c + 8 * hh);
+      if (!row_valid) raw = u32x4{0u, 0u, 0u, 0u};
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -143,115 +163,114 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
   for (int d = 0; d < C::DB; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-  float m_run = kNegInf;  // running max of raw scores of this lane's row
+  float m_run = kNegInf;  // running max of raw scores of this lane's row (possibly stale by < tau)
   float l_run = 0.f;      // running sum over this lane's half of the keys
 
-  u32x4 kreg[C::KCH];
-  u32x4 vreg[C::VCH];
-  const int64_t kv_row_stride = static_cast<int64_t>(a.hkv);
-  const int64_t kv_base_row = static_cast<int64_t>(b) * a.sk;
+  const int64_t kv_base = static_cast<int64_t>(b) * a.sk;
+  const int64_t last_key = a.sk - 1;
 
-  auto load_tile = [&](int t) {
+  // Direct global->LDS loads: wave-instruction i of this wave fills 64
+  // consecutive 16-byte chunk slots; each lane fetches the logical chunk that
+  // the swizzle maps to its slot.  Rows past the end of the block re-read the
+  // last key (finite values; their scores are masked).
+  const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
+  const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
+  const uint16_t* kbase = kg + kv_base * row_elems_k + kvh * DQK;
+  const uint16_t* vbase = vg + kv_base * row_elems_v + kvh * DV;
+  auto dma_k = [&](int t, int stage) {
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
+    const bool partial = key0 + kBN > a.sk;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / (DQK / 8);
-      const int cc = ci % (DQK / 8);
-      const int64_t key = key0 + row;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (key < a.sk)
-        raw = *reinterpret_cast<const u32x4*>(
-            kg + ((kv_base_row + key) * kv_row_stride + kvh) * DQK + cc * 8);
-      kreg[i] = raw;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / (DV / 8);
-      const int cc = ci % (DV / 8);
-      const int64_t key = key0 + row;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (key < a.sk)
-        raw = *reinterpret_cast<const u32x4*>(
-            vg + ((kv_base_row + key) * kv_row_stride + kvh) * DV + cc * 8);
-      vreg[i] = raw;
+    for (int i = 0; i < C::KDMA; ++i) {
+      const int p0 = (i * 4 + wave) * 64;
+      const int p = p0 + lane;
+      const int row = p / C::KCPR;
+      const int c = kswz<C::KCPR>(p % C::KCPR, row);
+      const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
+      __builtin_amdgcn_global_load_lds(
+          kbase + key * row_elems_k + c * 8,
+          (__attribute__((address_space(3))) void*)(Ks + stage * C::KTILE + p0 * 8), 16, 0, 0);
     }
   };
-  auto store_tile = [&]() {
+  auto dma_v = [&](int t, int stage) {
+    const int64_t key0 = static_cast<int64_t>(t) * kBN;
+    const bool partial = key0 + kBN > a.sk;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / (DQK / 8);
-      const int cc = ci % (DQK / 8);
-      *reinterpret_cast<u32x4*>(&Ks[row * C::KPITCH + cc * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / (DV / 8);
-      const int cc = ci % (DV / 8);
-      *reinterpret_cast<u32x4*>(&Vs[row * C::VPITCH + cc * 8]) = vreg[i];
+    for (int i = 0; i < C::VDMA; ++i) {
+      const int p0 = (i * 4 + wave) * 64;
+      const int p = p0 + lane;
+      const int row = p / C::VCPR;
+      const int c = vswz<C::VCPR>(p % C::VCPR, row);
+      const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
+      __builtin_amdgcn_global_load_lds(
+          vbase + key * row_elems_v + c * 8,
+          (__attribute__((address_space(3))) void*)(Vs + stage * C::VTILE + p0 * 8), 16, 0, 0);
     }
   };
 
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    // Rows of this wave that see no key of this tile skip the math.
-    const bool wave_has_rows = wq0 < a.sq;
-    const bool wave_sees_tile =
-        wave_has_rows && (!a.causal || a.k_pos0 + key0 <= a.q_pos0 + wq_last);
-    if (!wave_sees_tile) continue;
-    const bool need_mask = (key0 + kBN > a.sk) ||
-                           (a.causal && a.k_pos0 + key0 + kBN - 1 > a.q_pos0 + wq0);
-
-    // ---- S^T = K Q^T: two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* krow = &Ks[(kb * 32 + col) * C::KPITCH + 8 * hh];
-#pragma unroll
-      for (int c = 0; c < C::QC; ++c) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * c));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
-      }
-    }
-    // s[kb][i] is the score of key key0 + kb*32 + 8*(i/4) + 4*hh + i%4 for this lane's row.
-    if (need_mask) {
-      const int64_t qpos = a.q_pos0 + my_row;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = key0 + kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-          const bool vis = key < a.sk && (!a.causal || a.k_pos0 + key <= qpos);
-          if (!vis) s[kb][i] = kNegInf;
-        }
-    }
-
-    // ---- online softmax (exp2 domain)
-    float mx = kNegInf;
+  // One K fragment (A operand of S^T = K Q^T): key 32kb + col, d chunk 2c + hh.
+  auto k_frag = [&](const uint16_t* kst, int kb, int c) -> bf16x8 {
+    const int key = kb * 32 + col;
+    const int slot = kswz<C::KCPR>(2 * c + hh, key);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + (key * C::KCPR + slot) * 8));
+  };
+  // One V^T fragment (A operand of O^T += V^T P^T) for d_v block d and
+  // 16-key chunk kc, from row-major V through two transposed LDS reads.
+  auto v_frag = [&](const uint16_t* vst, int d, int kc) -> bf16x8 {
+    const int r0 = kc * 16 + 4 * (g >> 1) + (i16 >> 2);
+    const int r1 = r0 + 8;
+    const int cc = 4 * d + 2 * (g & 1) + ((i16 & 3) >> 1);
+    const int half = 4 * (i16 & 1);
+    const s16x4 lo = lds_read_tr16(vst + (r0 * C::VCPR + vswz<C::VCPR>(cc, r0)) * 8 + half);
+    const s16x4 hi = lds_read_tr16(vst + (r1 * C::VCPR + vswz<C::VCPR>(cc, r1)) * 8 + half);
+    return join_bf16x4(lo, hi);
+  };
+  // Scores of a whole tile: s[kb][i] is key 32kb + 8(i/4) + 4hh + i%4.
+  auto qk = [&](int stage, f32x16* s) {
+    const uint16_t* kst = Ks + stage * C::KTILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = wave_max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float neg_mc = -m_use * a.scale_log2;
-    const float alpha = fast_exp2(m_run * a.scale_log2 + neg_mc);  // 0 when m_run = -inf
-    m_run = m_new;
-
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C::QC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kst, kb, c), qf[c], s[kb], 0, 0, 0);
+  };
+  auto pv = [&](int stage, const bf16x8* pb) {
+    const uint16_t* vst = Vs + stage * C::VTILE;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vst, d, kc), pb[kc], oacc[d], 0, 0, 0);
+    // keep a few transposed reads in flight ahead of each MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+  auto mask_tile = [&](int t, f32x16* s) {
+    const int64_t key0 = static_cast<int64_t>(t) * kBN;
+    const bool need = (key0 + kBN > a.sk) ||
+                      (a.causal && a.k_pos0 + key0 + kBN - 1 > a.q_pos0 + wq0);
+    if (!need) return;
+    // visible iff local key < min(sk, qpos - k_pos0 + 1)
+    const int64_t lim64 = a.causal ? min(a.sk, qpos - a.k_pos0 + 1) : a.sk;
+    const int lim = static_cast<int>(max(min(lim64 - key0, static_cast<int64_t>(kBN)), static_cast<int64_t>(0)));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4) >= lim) s[kb][i] = kNegInf;
+  };
+  // Exponentials of one tile against the (possibly stale) running max, their
+  // sum, and P in bf16 for the PV product.
+  auto exps = [&](const f32x16* s, bf16x8* pb, float neg_mc) -> float {
     float psum = 0.f;
-    bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -262,27 +281,68 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
           psum += p;
           pb[kb * 2 + mm][e] = static_cast<__bf16>(p);
         }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int d = 0; d < C::DB; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+    return psum;
+  };
 
-    // ---- O^T += V^T P^T over four 16-key chunks
-    const int g = lane >> 4;   // 16-lane group
-    const int i16 = lane & 15;
+  if (ntiles > 0) {
+    f32x16 s_cur[2], s_nxt[2];
+    bf16x8 pb[4];
+    // prologue: K of tiles 0 and 1 and V of tile 0 in flight; scores of tile 0
+    dma_k(0, 0);
+    if (ntiles > 1) dma_k(1, 1);
+    dma_v(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(0, s_cur);
+    for (int j = 0; j < ntiles; ++j) {
+      // K_{j+1} and V_j have landed for every wave, and every wave is done
+      // with iteration j-1: K stage j%2 (held K_j) and V stage (j+1)%2 (held
+      // V_{j-1}) may be refilled.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 2 < ntiles) dma_k(j + 2, j & 1);
+      if (j + 1 < ntiles) dma_v(j + 1, (j + 1) & 1);
+      mask_tile(j, s_cur);
+
+      // Online softmax, exp2 domain.  Both halves of a row share m_run.  It is
+      // raised only when some row of the wave gained more than tau (log2
+      // units); otherwise the stale max stays, which is exact because
+      // numerator and denominator share it, and P stays below 2^tau.
+      float mx = kNegInf;
 #pragma unroll
-    for (int d = 0; d < C::DB; ++d) {
-      const int dvb = d * 32 + 16 * (g & 1);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int r0 = kc * 16 + 4 * (g >> 1) + (i16 >> 2);
-        const uint16_t* pa = &Vs[r0 * C::VPITCH + dvb + 4 * (i16 & 3)];
-        const s16x4 lo = lds_read_tr16(pa);
-        const s16x4 hi = lds_read_tr16(pa + 8 * C::VPITCH);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x4(lo, hi), pb[kc], oacc[d],
-                                                          0, 0, 0);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+      if (__ballot((mx - m_run) * a.scale_log2 > kTau) != 0) {   // false for -inf - -inf
+        const float full = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, full);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        m_run = m_new;
       }
+      const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
+      if (j + 1 < ntiles) {
+        // MFMA: scores of tile j+1, interleaved with the VALU exponentials of tile j
+        qk((j + 1) & 1, s_nxt);
+        l_run += exps(s_cur, pb, neg_mc);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::QC; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
+          if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        l_run += exps(s_cur, pb, neg_mc);
+      }
+      pv(j & 1, pb);                        // MFMA: O += P_j V_j
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
   }
 

@@ -15,5 +15,9 @@ def pytest_sessionstart(session):
     # build it only when nothing is there.
     lib = os.path.join(ROOT, "ring_attention_02_amd", "libringattn.so")
     if not os.path.exists(lib):
-        from ring_attention_02_amd.build import build
-        build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_ringattn_build", os.path.join(ROOT, "ring_attention_02_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
