@@ -1,0 +1,174 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+bench times, checked against the oracle on sampled outputs.
+
+Each sampled row of attention depends only on its own query row and the keys
+visible to it, so the oracle evaluated on those rows is exact for them.
+  C1  tiny non-causal ring, fp32: every row.
+  C2  zigzag rank 0, seq 8192, cp 4: every row of 6 of the 32 heads, plus
+      the restore index bit for bit.
+  C3  GQA decode over 8 shards, 64 x 131072: per-shard partials and merged
+      output of 3 whole requests (all heads).
+  C4  zigzag rank 0 of 1M tokens, cp 8: 640 (token, head) rows covering both
+      Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
+      few tokens.
+  C5  segmented chunked prefill (MLA shape): 544 (token, head) rows.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import host64, compare, say, F32_O, BF16_O, BF16_LSE
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import ring_attention_02_amd as ra
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return ra
+
+
+def _release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_c1_tiny_noncausal_ring(ra):
+    import workloads
+    from seeded_inputs import CONFIGS
+    c = CONFIGS[1]
+    shape = (c["batch"], c["seq"], c["heads"], c["d"])
+    q = workloads.host_tensor(1, 1, 0, shape, torch.float32)
+    k = workloads.host_tensor(1, 2, 0, shape, torch.float32)
+    v = workloads.host_tensor(1, 3, 0, shape, torch.float32)
+    o, lse = ra.noncausal_ring_sweep(q, k, v, c["n_blocks"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(host64(q), host64(k), host64(v), causal=False)
+    compare(host64(o), host64(lse), o_ref, lse_ref, F32_O, F32_O, "C1")
+
+
+def _sampled_rows_check(o, lse, q64_rows, k_of, v_of, q_pos, heads, groups, what,
+                        k_pos=None):
+    """Compare sampled (row, head) outputs: rows grouped by kv head.
+
+    q64_rows: [n, d] float64 query rows; heads: [n] query head of each row;
+    k_of(kvh) / v_of(kvh): float64 [Sk, d] keys / values of that kv head.
+    """
+    kvh_of = heads // groups
+    for kvh in np.unique(kvh_of):
+        sel = np.nonzero(kvh_of == kvh)[0]
+        kk, vv = k_of(int(kvh)), v_of(int(kvh))
+        pos = np.arange(kk.shape[0]) if k_pos is None else k_pos
+        ro, rl = oracle.attention_ref(q64_rows[sel][None, :, None, :], kk[None, :, None, :],
+                                      vv[None, :, None, :], q_pos[sel], pos, causal=True)
+        compare(o[sel], lse[sel], ro[0, :, 0], rl[0, :, 0], BF16_O, BF16_LSE,
+                f"{what} kv head {kvh} ({len(sel)} rows)")
+
+
+def test_c2_zigzag_full(ra):
+    import workloads
+    w = workloads.zigzag_setup(2)
+    ref_local, ref_restore = oracle.partition_ref([w["seq"]], w["cp"])
+    assert np.array_equal(w["local"], ref_local[w["rank"]])
+    assert np.array_equal(w["restore"], ref_restore)
+    graph = w["ring"].capture(w["q_local"], w["o"], w["lse"])     # the bench's launch mode
+    w["o"].fill_(5.0)
+    graph.replay()
+    torch.cuda.synchronize()
+    o, lse = host64(w["o"][0]), host64(w["lse"][0])
+    q, k, v = host64(w["q_local"][0]), host64(w["k_full"][0]), host64(w["v_full"][0])
+    q_pos = np.asarray(w["local"])
+    for h in (0, 5, 13, 20, 27, 31):
+        ro, rl = oracle.attention_ref(q[None, :, h:h + 1], k[None, :, h:h + 1], v[None, :, h:h + 1],
+                                      q_pos, np.arange(w["seq"]), causal=True)
+        compare(o[:, h], lse[:, h], ro[0, :, 0], rl[0, :, 0], BF16_O, BF16_LSE, f"C2 head {h}")
+    del w, graph
+    _release()
+
+
+def test_c3_decode_full(ra):
+    import workloads
+    w = workloads.decode_setup()
+    o_parts, lse_parts = ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"])
+    o, lse = ra.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    dev_ref, slot_ref = oracle.slot_mapping_ref(np.arange(w["ctx"]), 128, 16, 8, 1)
+    assert np.array_equal(w["dev"], dev_ref) and np.array_equal(w["slot"], slot_ref)
+    q64 = host64(w["q"])
+    for b in (0, 37, 63):
+        kc, vc = workloads.decode_context(b)
+        k64, v64 = host64(kc)[None], host64(vc)[None]
+        del kc, vc
+        po, pl, mo, ml = oracle.decode_shards_ref(q64[b:b + 1], k64, v64, dev_ref, w["n_shards"])
+        compare(host64(o_parts[:, b]), host64(lse_parts[:, b]), po[:, 0], pl[:, 0], BF16_O,
+                BF16_LSE, f"C3 request {b} shard partials")
+        compare(host64(o[b]), host64(lse[b]), mo[0], ml[0], BF16_O, BF16_LSE, f"C3 request {b}")
+    del w
+    _release()
+
+
+def test_c4_long_zigzag_sampled(ra):
+    import workloads
+    w = workloads.zigzag_setup(4)
+    w["ring"].run(w["q_local"], w["o"], w["lse"])
+    torch.cuda.synchronize()
+    c, hq, hkv = w["chunk"], w["hq"], w["hkv"]
+    n_local = w["q_local"].shape[1]
+    rng = np.random.default_rng(4)
+    toks = {0, 1, 63, 64, 127, 128, c - 1, c, c + 1, c + 63, c + 64, 2 * c - 1, c // 2}
+    toks |= set(rng.integers(0, n_local, 30).tolist())
+    rows = []
+    for t in sorted(toks):
+        for h in rng.choice(hq, 8, replace=False):
+            rows.append((t, int(h)))
+    for t in (0, c - 1, 2 * c - 1):            # every head of a few tokens
+        rows += [(t, h) for h in range(hq)]
+    rows = sorted(set(rows))
+    assert len(rows) >= 512
+    tt = np.array([r[0] for r in rows])
+    hh = np.array([r[1] for r in rows])
+    ti, hi = torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()
+    o = host64(w["o"][0][ti, hi])
+    lse = host64(w["lse"][0][ti, hi])
+    q_rows = host64(w["q_local"][0][ti, hi])
+    q_pos = np.asarray(w["local"])[tt]
+    say(f"C4: {len(rows)} sampled rows")
+    k_full, v_full = w["k_full"], w["v_full"]
+    _sampled_rows_check(o, lse, q_rows, lambda g: host64(k_full[0, :, g]),
+                        lambda g: host64(v_full[0, :, g]), q_pos, hh, hq // hkv, "C4")
+    del w, k_full, v_full
+    _release()
+
+
+def test_c5_segmented_sampled(ra):
+    import workloads
+    w = workloads.segmented_setup()
+    ra.segmented_prefill(w["q"], w["k"], w["v"], w["o"], w["lse"], q_pos0=w["q_pos0"],
+                         segment=w["segment"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    sq, h = w["sq"], w["h"]
+    heads = rng.choice(h, 16, replace=False)
+    rows = []
+    for hd in heads:
+        toks = {0, 1, 63, 64, 127, sq - 1, sq // 2} | set(rng.integers(0, sq, 27).tolist())
+        rows += [(t, int(hd)) for t in sorted(toks)]
+    rows = sorted(set(rows))
+    assert len(rows) >= 512
+    tt = np.array([r[0] for r in rows])
+    hh = np.array([r[1] for r in rows])
+    ti, hi = torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()
+    o = host64(w["o"][0][ti, hi])
+    lse = host64(w["lse"][0][ti, hi])
+    q_rows = host64(w["q"][0][ti, hi])
+    q_pos = w["q_pos0"] + tt
+    say(f"C5: {len(rows)} sampled rows")
+    k, v = w["k"], w["v"]
+    _sampled_rows_check(o, lse, q_rows, lambda g: host64(k[0, :, g]), lambda g: host64(v[0, :, g]),
+                        q_pos, hh, 1, "C5")
+    del w, k, v
+    _release()

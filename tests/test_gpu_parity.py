@@ -254,3 +254,25 @@ def test_zigzag_graph_replay_matches_eager(ra):
         ring.run(q_local, o, lse)        # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(o, o_eager)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_peaked_scores_exercise_max_raises(ra, causal):
+    """Large score range (queries scaled x8, some keys planted equal to a
+    query): the running max is raised many times inside a block, and the
+    result must still match the oracle."""
+    sq, sk, hq, hkv, d = 200, 700, 4, 2, 128
+    q, _ = tensor(61, 1, 0, (1, sq, hq, d), torch.float32)
+    k, _ = tensor(61, 2, 0, (1, sk, hkv, d), torch.float32)
+    v, _ = tensor(61, 3, 0, (1, sk, hkv, d), torch.bfloat16)
+    q = q * 8.0
+    k[0, 650:660, 0] = q[0, 190:200, 0] / 8.0       # very large scores late in the block
+    k[0, 3, 1] = q[0, 5, 2] / 8.0
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o = torch.empty((1, sq, hq, d), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    ra.ring_attn_step(qb, kb, v, o, lse, q_pos0=600, k_pos0=0, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(host64(qb), host64(kb), host64(v), 600 + np.arange(sq),
+                                          np.arange(sk), causal)
+    compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "peaked")
