@@ -40,7 +40,22 @@ def parse():
     p.add_argument("--primary-only", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of secondary workloads to run")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 28                      # 2^28 float32 = 1 GiB
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device-to-device copy", "bytes_read": n * 4,
+                      "bytes_written": n * 4, "launches": 5}), flush=True)
 
 
 def log(msg):
@@ -112,6 +127,25 @@ def time_steps(step_fn, steps, warmup):
         step_fn()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def profiled_traffic(summary, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source changed after the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(root, "profiles", summary)).read()
+        src = open(os.path.join(root, "ring_attention_02_amd", "csrc", source), "rb").read()
+    except OSError:
+        return None
+    sha = hashlib.sha256(src).hexdigest()[:16]
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and
+                  line.split(": ", 1)[0] in ("kernel source sha256 prefix (attn_step.hip)",
+                                              "traffic_bytes_per_launch"))
+    if fields.get("kernel source sha256 prefix (attn_step.hip)", "").strip() != sha:
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
 
 
 def roofline_entry(bound, achieved, peak, unit, traffic=None):
@@ -257,6 +291,9 @@ def main():
     import torch
     import ring_attention_02_amd  # noqa: F401  (fails loudly if the library is missing)
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
     w2, sec2, l2 = zigzag_bench(2, args.steps, args.warmup)
@@ -271,7 +308,9 @@ def main():
                                "d 128, bf16",
                    "global_batch": 1, "seq_len": 8192, "parallelism": "cp4 ring emulated on 1 GPU",
                    "flops_per_step": w2["flops"]},
-        "roofline": roofline_entry("mfma", l2["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "roofline": roofline_entry("mfma", l2["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                                   profiled_traffic("attn_step_bf16_zigzag_seq8192_cp4.md",
+                                                    "attn_step.hip")),
         "kernel": {"name": "attn_step_bf16_kernel<128,128>",
                    "mean_launch_ms": round(l2["mean_launch_ms"], 5),
                    "launches_per_step": l2["launches_per_step"],
