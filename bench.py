@@ -94,27 +94,15 @@ def kernel_launch_stats(launch_list, reps):
 
 
 def zigzag_launches(w, cls_filter=None):
-    """The non-SKIP ring_attn_step launches of one zigzag sweep (K/V read in place)."""
-    import ring_attention_02_amd as ra
-    ring, q, o, lse, c = w["ring"], w["q_local"], w["o"], w["lse"], w["chunk"]
-    out = []
-    first = [True, True]
-    for t, kv_parts in enumerate(ring.steps):
-        ks, vs = ring.local_slices(t)
-        for qi, qp in enumerate(ring.q_parts):
-            qs = slice(qi * c, (qi + 1) * c)
-            for kj, kp in enumerate(kv_parts):
-                cls = ra.classify(qp * c, c, kp * c, c, True)
-                acc = not first[qi]
-                first[qi] = False
-                if cls == ra.SKIP and acc:
-                    continue
-                if cls_filter is not None and cls != cls_filter:
-                    continue
-                out.append(lambda a=(q[:, qs], ks[kj], vs[kj], o[:, qs], lse[:, qs]),
-                           k=dict(q_pos0=qp * c, k_pos0=kp * c, causal=True, accumulate=acc):
-                           ra.ring_attn_step(*a, **k))
-    return out
+    """The ring_attn_step launches of one zigzag sweep, exactly as the ring issues
+    them (collected from the sweep itself; K/V slots hold the staged data)."""
+    import torch
+    launches = []
+    w["ring"].run(w["q_local"], w["o"], w["lse"],
+                  on_launch=lambda t, qi, kj, cls, fn: launches.append((cls, fn)))
+    torch.cuda.synchronize()
+    # SKIP pairs launch no attention kernel
+    return [fn for cls, fn in launches if cls != 2 and (cls_filter is None or cls == cls_filter)]
 
 
 def time_steps(step_fn, steps, warmup):

@@ -28,8 +28,9 @@
  *     (except CP_EHIP, reported after a launch failed).  A short detail
  *     string for the calling thread is available from cp_last_error().
  *   - The library never prints, never throws across this boundary, keeps no
- *     global mutable state besides the thread-local error string, and
- *     allocates no device memory: the caller owns every buffer.
+ *     global mutable state besides the thread-local error string and a
+ *     per-device cache of the compute-unit count, and allocates no device
+ *     memory: the caller owns every buffer.
  *   - Host functions are synchronous and take host pointers.  Device
  *     functions take device pointers (16-byte aligned, densely packed in the
  *     layouts stated), are asynchronous on `stream` (a hipStream_t passed as
@@ -202,6 +203,20 @@ int32_t split_kv_decode(const void* q, const void* k_shards, const void* v_shard
                         const int64_t* shard_lens, int32_t hq, int32_t hkv, int32_t d_qk,
                         int32_t d_v, float scale, float* o_parts, float* lse_parts,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ring_stage_copy -- receive a ring step's K/V block into a staging slot.
+ * [RA] ring-topology excerpt (each step a device takes over the K/V block of
+ * its predecessor while computing); [VID] chapter on the wire budget and
+ * double buffering.  On one GPU the transfer is a device-to-device copy.
+ *
+ *   dsts, srcs  host arrays of n device pointers (16-byte aligned).
+ *   bytes       host array of n byte counts (multiples of 16).
+ * Copies piece i from srcs[i] to dsts[i] for all 1 <= n <= 8 pieces in one
+ * launch, asynchronously on `stream`.  Pieces must not overlap each other.
+ * ---------------------------------------------------------------------- */
+int32_t ring_stage_copy(void* const* dsts, const void* const* srcs, const int64_t* bytes,
+                        int32_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ ABI_VERSION = 1
 # Every symbol include/ringattn.h declares.
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
-            "split_kv_decode_workspace", "split_kv_decode")
+            "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy")
 
 
 class RingAttnError(RuntimeError):
@@ -64,6 +64,8 @@ _lib.split_kv_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
 _lib.split_kv_decode.restype = _i32
 _lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i32, _i32, _i32,
                                  _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+_lib.ring_stage_copy.restype = _i32
+_lib.ring_stage_copy.argtypes = [_vp, _vp, _vp, _i32, _vp]
 
 if _lib.cp_abi_version() != ABI_VERSION:
     raise ImportError(f"libringattn ABI {_lib.cp_abi_version()} != binding ABI {ABI_VERSION}")
@@ -247,9 +249,24 @@ def split_kv_decode(q, k_shards, v_shards, shard_lens=None, scale=None, o_parts=
     return o_parts, lse_parts
 
 
+def stage_copy(pairs, stream=None):
+    """Copy each (dst, src) pair of equally sized contiguous GPU tensors in one launch."""
+    n = len(pairs)
+    dsts = (ctypes.c_void_p * n)()
+    srcs = (ctypes.c_void_p * n)()
+    nbytes = (ctypes.c_int64 * n)()
+    for i, (dst, src) in enumerate(pairs):
+        if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+            raise ValueError("stage_copy: piece sizes differ")
+        dsts[i] = _dev_ptr(dst, "dst").value
+        srcs[i] = _dev_ptr(src, "src").value
+        nbytes[i] = dst.numel() * dst.element_size()
+    _check(_lib.ring_stage_copy(dsts, srcs, nbytes, n, _stream_handle(stream)), "ring_stage_copy")
+
+
 from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E402
 
-__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "lse_merge",
+__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "lse_merge", "stage_copy",
            "split_kv_decode", "split_kv_decode_workspace", "ZigzagRing", "segmented_prefill",
            "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
            "last_error"]

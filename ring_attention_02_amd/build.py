@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
 
-SOURCES = ["api.cpp", "host_index.cpp", "attn_step.hip", "lse_merge.hip", "decode.hip"]
+SOURCES = ["api.cpp", "host_index.cpp", "attn_step.hip", "lse_merge.hip", "decode.hip", "stage.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -25,6 +25,8 @@
 //  * exp2-domain online softmax; fully visible tiles skip the mask.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kernels_common.h"
 #include "status.h"
 
@@ -105,15 +107,25 @@ __device__ __forceinline__ int vswz(int c, int r) {
   else return c ^ (4 * ((r >> 1) & 1));                // rows of 128 bytes
 }
 
-template <int DQK, int DV>
-__global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a) {
+// SPLIT = 2 doubles the waves of a workgroup: waves 4-7 sweep the odd key
+// tiles of the same 128 query rows while waves 0-3 sweep the even ones, and
+// the two softmax states are merged through LDS at the end.  This keeps two
+// waves per SIMD even when a launch has only one workgroup per CU.
+template <int DQK, int DV, int SPLIT>
+__global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(StepArgs a) {
   using C = Bf16Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * C::VTILE];
+  // K stages of both halves, then V stages of both halves.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SPLIT * 2 * (C::KTILE + C::VTILE)];
+  uint16_t* const Ks = smem;
+  uint16_t* const Vs = smem + SPLIT * 2 * C::KTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_all & 3;                  // wave within its half: owns 32 query rows
+  const int half = SPLIT == 1 ? 0 : wave_all >> 2;  // which alternate key tiles it sweeps
+  uint16_t* const Kh = Ks + half * 2 * C::KTILE;
+  uint16_t* const Vh = Vs + half * 2 * C::VTILE;
   const int col = lane & 31;  // query row within the wave (B / C column)
   const int hh = lane >> 5;   // which half of each contraction slice this lane holds
   const int g = lane >> 4;    // 16-lane group (transposed V reads)
@@ -189,7 +201,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
       const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
       __builtin_amdgcn_global_load_lds(
           kbase + key * row_elems_k + c * 8,
-          (__attribute__((address_space(3))) void*)(Ks + stage * C::KTILE + p0 * 8), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(Kh + stage * C::KTILE + p0 * 8), 16, 0, 0);
     }
   };
   auto dma_v = [&](int t, int stage) {
@@ -204,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
       const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
       __builtin_amdgcn_global_load_lds(
           vbase + key * row_elems_v + c * 8,
-          (__attribute__((address_space(3))) void*)(Vs + stage * C::VTILE + p0 * 8), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(Vh + stage * C::VTILE + p0 * 8), 16, 0, 0);
     }
   };
 
@@ -227,7 +239,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
   };
   // Scores of a whole tile: s[kb][i] is key 32kb + 8(i/4) + 4hh + i%4.
   auto qk = [&](int stage, f32x16* s) {
-    const uint16_t* kst = Ks + stage * C::KTILE;
+    const uint16_t* kst = Kh + stage * C::KTILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kst, kb, c), qf[c], s[kb], 0, 0, 0);
   };
   auto pv = [&](int stage, const bf16x8* pb) {
-    const uint16_t* vst = Vs + stage * C::VTILE;
+    const uint16_t* vst = Vh + stage * C::VTILE;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -284,66 +296,106 @@ __global__ void __launch_bounds__(kThreads, 2) attn_step_bf16_kernel(StepArgs a)
     return psum;
   };
 
-  if (ntiles > 0) {
+  // This half sweeps tiles half, half + SPLIT, ...: my_n of them.  Every wave
+  // runs the same number of iterations (barriers stay uniform); a half with
+  // fewer tiles idles through its last one.
+  const int my_n = ntiles > half ? (ntiles - half + SPLIT - 1) / SPLIT : 0;
+  const int n_iter = (ntiles + SPLIT - 1) / SPLIT;
+  auto tile = [&](int j) { return j * SPLIT + half; };
+  if (n_iter > 0) {
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 pb[4];
-    // prologue: K of tiles 0 and 1 and V of tile 0 in flight; scores of tile 0
-    dma_k(0, 0);
-    if (ntiles > 1) dma_k(1, 1);
-    dma_v(0, 0);
+    // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight; scores of tile 0
+    if (my_n > 0) dma_k(tile(0), 0);
+    if (my_n > 1) dma_k(tile(1), 1);
+    if (my_n > 0) dma_v(tile(0), 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    qk(0, s_cur);
-    for (int j = 0; j < ntiles; ++j) {
+    if (my_n > 0) qk(0, s_cur);
+    for (int j = 0; j < n_iter; ++j) {
       // K_{j+1} and V_j have landed for every wave, and every wave is done
       // with iteration j-1: K stage j%2 (held K_j) and V stage (j+1)%2 (held
       // V_{j-1}) may be refilled.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (j + 2 < ntiles) dma_k(j + 2, j & 1);
-      if (j + 1 < ntiles) dma_v(j + 1, (j + 1) & 1);
-      mask_tile(j, s_cur);
+      if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);
+      if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);
+      if (j < my_n) {
+        mask_tile(tile(j), s_cur);
 
-      // Online softmax, exp2 domain.  Both halves of a row share m_run.  It is
-      // raised only when some row of the wave gained more than tau (log2
-      // units); otherwise the stale max stays, which is exact because
-      // numerator and denominator share it, and P stays below 2^tau.
-      float mx = kNegInf;
+        // Online softmax, exp2 domain.  Both halves of a row share m_run.  It
+        // is raised only when some row of the wave gained more than tau (log2
+        // units); otherwise the stale max stays, which is exact because
+        // numerator and denominator share it, and P stays below 2^tau.
+        float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
-      if (__ballot((mx - m_run) * a.scale_log2 > kTau) != 0) {   // false for -inf - -inf
-        const float full = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, full);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 when m_run = -inf
-        l_run *= alpha;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+        if (__ballot((mx - m_run) * a.scale_log2 > kTau) != 0) {   // false for -inf - -inf
+          const float full = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run, full);
+          const float m_use = m_new == kNegInf ? 0.f : m_new;
+          const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 when m_run = -inf
+          l_run *= alpha;
 #pragma unroll
-        for (int d = 0; d < C::DB; ++d)
+          for (int d = 0; d < C::DB; ++d)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
-      if (j + 1 < ntiles) {
-        // MFMA: scores of tile j+1, interleaved with the VALU exponentials of tile j
-        qk((j + 1) & 1, s_nxt);
-        l_run += exps(s_cur, pb, neg_mc);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * C::QC; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
-          if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+          m_run = m_new;
         }
-      } else {
-        l_run += exps(s_cur, pb, neg_mc);
-      }
-      pv(j & 1, pb);                        // MFMA: O += P_j V_j
+        const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
+        if (j + 1 < my_n) {
+          // MFMA: scores of tile j+1, interleaved with the VALU exponentials of tile j
+          qk((j + 1) & 1, s_nxt);
+          l_run += exps(s_cur, pb, neg_mc);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+          for (int i = 0; i < 2 * C::QC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
+            if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else {
+          l_run += exps(s_cur, pb, neg_mc);
+        }
+        pv(j & 1, pb);                        // MFMA: O += P_j V_j
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+      }
     }
+  }
+
+  if constexpr (SPLIT == 2) {
+    // Fold the odd-tile half into the even-tile half, lane by lane (same query
+    // row, same key half hh): the K/V stages are free now and hold the states.
+    __syncthreads();
+    float* xs = reinterpret_cast<float*>(smem);   // [wave][16*DB + 2][64 lanes]
+    constexpr int NV = 16 * C::DB + 2;
+    static_assert(4 * NV * 64 * sizeof(float) <= sizeof(smem), "merge buffer fits the stages");
+    float* mine = xs + wave * NV * 64 + lane;
+    if (half == 1) {
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mine[(16 * d + i) * 64] = oacc[d][i];
+      mine[(NV - 2) * 64] = m_run;
+      mine[(NV - 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = mine[(NV - 2) * 64];
+    const float l1 = mine[(NV - 1) * 64];
+    const float m = fmaxf(m_run, m1);
+    const float m_use = m == kNegInf ? 0.f : m;
+    const float a0 = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 for an empty side
+    const float a1 = fast_exp2((m1 - m_use) * a.scale_log2);
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[d][i] = oacc[d][i] * a0 + mine[(16 * d + i) * 64] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
 
   // ---- epilogue: normalise, LSE, optional merge into the running result
@@ -511,6 +563,32 @@ int32_t launch(Kernel kernel, int rows_per_wg, int threads, StepArgs args, int64
   return CP_OK;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cached[64];   // 0 = not queried yet; the value never changes
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+// bf16 launch: a grid with fewer than two 4-wave workgroups per CU runs the
+// 8-wave key-split variant so every SIMD still holds two waves.
+template <int DQK, int DV>
+int32_t launch_bf16(StepArgs args, int64_t batch, hipStream_t stream) {
+  const int64_t wgs = (args.sq + kBM - 1) / kBM * args.hq * batch;
+  if constexpr (DQK <= 128) {
+    if (wgs < 2 * static_cast<int64_t>(device_cus()))
+      return launch(attn_step_bf16_kernel<DQK, DV, 2>, kBM, 2 * kThreads, args, batch, stream);
+  }
+  return launch(attn_step_bf16_kernel<DQK, DV, 1>, kBM, kThreads, args, batch, stream);
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -571,11 +649,11 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
       int32_t rc;
       if (dtype == CP_BF16) {
         if (d_qk == 64)
-          rc = launch(attn_step_bf16_kernel<64, 64>, kBM, kThreads, args, batch, st);
+          rc = launch_bf16<64, 64>(args, batch, st);
         else if (d_qk == 128)
-          rc = launch(attn_step_bf16_kernel<128, 128>, kBM, kThreads, args, batch, st);
+          rc = launch_bf16<128, 128>(args, batch, st);
         else
-          rc = launch(attn_step_bf16_kernel<192, 128>, kBM, kThreads, args, batch, st);
+          rc = launch_bf16<192, 128>(args, batch, st);
       } else {
         if (d_qk == 64)
           rc = launch(attn_step_f32_kernel<64, 64>, kF32Rows, kF32Rows, args, batch, st);

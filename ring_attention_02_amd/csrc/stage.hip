@@ -1,0 +1,72 @@
+// Ring-step staging: "receiving" the next K/V block into a staging slot.
+//
+// In the ring (guijiagi.com "Ring Attention", ring-topology excerpt) every
+// step hands the current K/V block to the next device while the local
+// attention runs, and the video "How Context Parallelism Splits Long
+// Sequences Across GPUs" (chapter on the wire budget) double-buffers that
+// transfer.  On one GPU the transfer is a device-to-device copy of the
+// block's pieces into the idle slot; this kernel moves all of them in one
+// launch (16-byte vector loads and stores, grid-stride over the total).
+#include <hip/hip_runtime.h>
+
+#include "kernels_common.h"
+#include "status.h"
+
+namespace ringattn {
+namespace {
+
+constexpr int kMaxPieces = 8;
+constexpr int kStageThreads = 256;
+
+struct StagePieces {
+  u32x4* dst[kMaxPieces];
+  const u32x4* src[kMaxPieces];
+  int64_t end[kMaxPieces];   // exclusive prefix sums of the pieces' 16-B units
+  int32_t n;
+};
+
+__global__ void __launch_bounds__(kStageThreads) stage_copy_kernel(StagePieces p) {
+  const int64_t total = p.end[p.n - 1];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStageThreads;
+  int piece = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; i < total; i += stride) {
+    while (i >= p.end[piece]) ++piece;                // indices only grow
+    const int64_t local = i - (piece == 0 ? 0 : p.end[piece - 1]);
+    p.dst[piece][local] = p.src[piece][local];
+  }
+}
+
+}  // namespace
+}  // namespace ringattn
+
+extern "C" int32_t ring_stage_copy(void* const* dsts, const void* const* srcs,
+                                   const int64_t* bytes, int32_t n, void* stream) {
+  using namespace ringattn;
+  RA_CHECK(n >= 1 && n <= kMaxPieces, CP_EINVAL, "ring_stage_copy: n=%d outside [1, %d]", n,
+           kMaxPieces);
+  RA_CHECK(dsts && srcs && bytes, CP_EINVAL, "ring_stage_copy: NULL array");
+  StagePieces p{};
+  p.n = n;
+  int64_t units = 0;
+  for (int i = 0; i < n; ++i) {
+    RA_CHECK(bytes[i] >= 0 && bytes[i] % 16 == 0, CP_EINVAL,
+             "ring_stage_copy: piece %d has %lld bytes (must be a non-negative multiple of 16)", i,
+             static_cast<long long>(bytes[i]));
+    RA_CHECK(bytes[i] == 0 || (dsts[i] && srcs[i]), CP_EINVAL, "ring_stage_copy: NULL piece %d", i);
+    RA_CHECK((reinterpret_cast<uintptr_t>(dsts[i]) & 15u) == 0 &&
+                 (reinterpret_cast<uintptr_t>(srcs[i]) & 15u) == 0,
+             CP_EINVAL, "ring_stage_copy: piece %d is not 16-byte aligned", i);
+    p.dst[i] = static_cast<u32x4*>(dsts[i]);
+    p.src[i] = static_cast<const u32x4*>(srcs[i]);
+    units += bytes[i] / 16;
+    p.end[i] = units;
+  }
+  if (units == 0) return ok();
+  const int64_t want = (units + kStageThreads * 4 - 1) / (kStageThreads * 4);
+  const unsigned blocks = static_cast<unsigned>(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(blocks), dim3(kStageThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
+  const hipError_t err = hipGetLastError();
+  RA_CHECK(err == hipSuccess, CP_EHIP, "ring_stage_copy: launch failed: %s", hipGetErrorString(err));
+  return ok();
+}

@@ -20,7 +20,7 @@ block in place.
 
 import math
 
-from . import ring_attn_step, lse_merge, classify, FULL, DIAG, SKIP
+from . import ring_attn_step, lse_merge, classify, stage_copy, FULL, DIAG, SKIP
 
 
 def _torch():
@@ -68,10 +68,8 @@ class ZigzagRing:
         if self.pending_free[slot]:
             self.side.wait_event(self.free[slot])
         ks, vs = self.local_slices(t)
-        with torch.cuda.stream(self.side):
-            for j in range(2):
-                self.kbuf[slot][j].copy_(ks[j], non_blocking=True)
-                self.vbuf[slot][j].copy_(vs[j], non_blocking=True)
+        stage_copy([(self.kbuf[slot][0], ks[0]), (self.kbuf[slot][1], ks[1]),
+                    (self.vbuf[slot][0], vs[0]), (self.vbuf[slot][1], vs[1])], stream=self.side)
         self.ready[slot].record(self.side)
 
     def pairs(self):
@@ -107,16 +105,27 @@ class ZigzagRing:
                 self._stage(t + 1)
             for qi, qp in enumerate(self.q_parts):
                 qs = slice(qi * c, (qi + 1) * c)
-                for kj, kp in enumerate(kv_parts):
+                classes = [classify(qp * c, c, kp * c, c, True) for kp in kv_parts]
+                if t > 0 and classes == [FULL, FULL]:
+                    # Both staged parts are wholly visible and sit side by side
+                    # in the slot: one launch over 2c keys (no mask needed).
+                    groups = [(0, 2, False, FULL)]
+                else:
+                    groups = [(kj, kj + 1, True, classes[kj]) for kj in range(2)]
+                for k0, k1, causal, cls in groups:
                     acc = not first[qi]
-                    args = (q_local[:, qs], ks[kj], vs[kj], o[:, qs], lse[:, qs])
-                    kw = dict(q_pos0=qp * c, k_pos0=kp * c, causal=True, scale=scale,
-                              accumulate=acc)
+                    if t > 0:
+                        kk = self.kbuf[t % 2][k0:k1].view(1, (k1 - k0) * c, *ks.shape[3:])
+                        vv = self.vbuf[t % 2][k0:k1].view(1, (k1 - k0) * c, *vs.shape[3:])
+                    else:
+                        kk, vv = ks[k0], vs[k0]
+                    args = (q_local[:, qs], kk, vv, o[:, qs], lse[:, qs])
+                    kw = dict(q_pos0=qp * c, k_pos0=kv_parts[k0] * c, causal=causal,
+                              scale=scale, accumulate=acc)
                     if on_launch is None:
                         ring_attn_step(*args, **kw)
                     else:
-                        cls = classify(qp * c, c, kp * c, c, True)
-                        on_launch(t, qi, kj, cls, lambda a=args, k=kw: ring_attn_step(*a, **k))
+                        on_launch(t, qi, k0, cls, lambda a=args, k=kw: ring_attn_step(*a, **k))
                     first[qi] = False
             if t >= 1:
                 self.free[t % 2].record(main)

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
@@ -160,3 +160,18 @@ def test_device_calls_validate_before_launch(ra):
     assert lib.split_kv_decode(fake, fake, fake, 0, 1, 1, 8192, None, 8, 1, 128, 128, 0.1,
                                fake, fake, None, 0, None) == ra.CP_EINVAL  # workspace missing
     assert lib.split_kv_decode_workspace(8, 64, 64, 8, 128, 16384) == 0
+
+
+def test_stage_copy_validates_before_launch(ra):
+    lib = ra.lib()
+    n = 2
+    dsts = (ctypes.c_void_p * n)(256, 512)
+    srcs = (ctypes.c_void_p * n)(1024, 2048)
+    good = (ctypes.c_int64 * n)(32, 64)
+    odd = (ctypes.c_int64 * n)(32, 63)
+    assert lib.ring_stage_copy(dsts, srcs, good, 0, None) == ra.CP_EINVAL
+    assert lib.ring_stage_copy(dsts, srcs, good, 9, None) == ra.CP_EINVAL
+    assert lib.ring_stage_copy(dsts, srcs, odd, 2, None) == ra.CP_EINVAL
+    misaligned = (ctypes.c_void_p * n)(256, 520)
+    assert lib.ring_stage_copy(misaligned, srcs, good, 2, None) == ra.CP_EINVAL
+    assert lib.ring_stage_copy(None, srcs, good, 2, None) == ra.CP_EINVAL

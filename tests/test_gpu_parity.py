@@ -276,3 +276,15 @@ def test_peaked_scores_exercise_max_raises(ra, causal):
     o_ref, lse_ref = oracle.attention_ref(host64(qb), host64(kb), host64(v), 600 + np.arange(sq),
                                           np.arange(sk), causal)
     compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "peaked")
+
+
+def test_stage_copy_pieces(ra):
+    src = [torch.randn(n, device="cuda") for n in (4096, 4, 100000 * 4, 12)]
+    dst = [torch.full_like(x, -1.0) for x in src]
+    big = torch.randn((2, 1000, 8, 128), device="cuda").to(torch.bfloat16)
+    big_dst = torch.zeros_like(big)
+    ra.stage_copy(list(zip(dst, src)) + [(big_dst[0], big[1]), (big_dst[1], big[0])])
+    torch.cuda.synchronize()
+    for d, s_ in zip(dst, src):
+        assert torch.equal(d, s_)
+    assert torch.equal(big_dst[0], big[1]) and torch.equal(big_dst[1], big[0])
