@@ -86,6 +86,8 @@ struct Bf16Cfg {
   static constexpr int VTILE = kBN * DV;             // bf16 elements of one V stage
   static constexpr int KDMA = kBN * KCPR / kThreads;  // 16-B direct loads per thread per K tile
   static constexpr int VDMA = kBN * VCPR / kThreads;
+  static constexpr int KROWS_PER_DMA = kThreads / KCPR;  // K rows one block-wide direct load fills
+  static constexpr int VROWS_PER_DMA = kThreads / VCPR;
   static constexpr int QC = DQK / 16;  // MFMA steps of S^T = K Q^T
   static constexpr int DB = DV / 32;   // 32-row d_v blocks of O^T
   static_assert(KDMA * kThreads == kBN * KCPR && VDMA * kThreads == kBN * VCPR, "tile split");
@@ -189,34 +191,63 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
   const uint16_t* kbase = kg + kv_base * row_elems_k + kvh * DQK;
   const uint16_t* vbase = vg + kv_base * row_elems_v + kvh * DV;
+  // Per-lane element offset of this lane's first direct load inside a tile
+  // (loop-invariant).  With 8 or 16 chunks per row, instruction i lands
+  // 256/CPR rows further down and the swizzle (which reads only the low row
+  // bits) is unchanged, so instruction i adds a uniform number of rows.
+  uint32_t koff0 = 0, voff0 = 0;
+  {
+    const int p = wave * 64 + lane;
+    const int kr = p / C::KCPR;
+    koff0 = static_cast<uint32_t>(kr * row_elems_k + kswz<C::KCPR>(p % C::KCPR, kr) * 8);
+    const int vr = p / C::VCPR;
+    voff0 = static_cast<uint32_t>(vr * row_elems_v + vswz<C::VCPR>(p % C::VCPR, vr) * 8);
+  }
+  constexpr bool kUniformStep = C::KCPR == 8 || C::KCPR == 16;
+  const int64_t kstep = C::KROWS_PER_DMA * row_elems_k;   // elements between direct loads
+  const int64_t vstep = C::VROWS_PER_DMA * row_elems_v;
   auto dma_k = [&](int t, int stage) {
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const bool partial = key0 + kBN > a.sk;
+    uint16_t* dst = Kh + stage * C::KTILE;
+    if (kUniformStep && key0 + kBN <= a.sk) {
+      const uint16_t* base = kbase + key0 * row_elems_k;
 #pragma unroll
-    for (int i = 0; i < C::KDMA; ++i) {
-      const int p0 = (i * 4 + wave) * 64;
-      const int p = p0 + lane;
-      const int row = p / C::KCPR;
-      const int c = kswz<C::KCPR>(p % C::KCPR, row);
-      const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
-      __builtin_amdgcn_global_load_lds(
-          kbase + key * row_elems_k + c * 8,
-          (__attribute__((address_space(3))) void*)(Kh + stage * C::KTILE + p0 * 8), 16, 0, 0);
+      for (int i = 0; i < C::KDMA; ++i)
+        __builtin_amdgcn_global_load_lds(base + i * kstep + koff0,
+            (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KDMA; ++i) {
+        const int p0 = (i * 4 + wave) * 64;
+        const int p = p0 + lane;
+        const int row = p / C::KCPR;
+        const int c = kswz<C::KCPR>(p % C::KCPR, row);
+        const int64_t key = min(key0 + row, last_key);
+        __builtin_amdgcn_global_load_lds(kbase + key * row_elems_k + c * 8,
+            (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, 0, 0);
+      }
     }
   };
   auto dma_v = [&](int t, int stage) {
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const bool partial = key0 + kBN > a.sk;
+    uint16_t* dst = Vh + stage * C::VTILE;
+    if (key0 + kBN <= a.sk) {
+      const uint16_t* base = vbase + key0 * row_elems_v;
 #pragma unroll
-    for (int i = 0; i < C::VDMA; ++i) {
-      const int p0 = (i * 4 + wave) * 64;
-      const int p = p0 + lane;
-      const int row = p / C::VCPR;
-      const int c = vswz<C::VCPR>(p % C::VCPR, row);
-      const int64_t key = partial ? min(key0 + row, last_key) : key0 + row;
-      __builtin_amdgcn_global_load_lds(
-          vbase + key * row_elems_v + c * 8,
-          (__attribute__((address_space(3))) void*)(Vh + stage * C::VTILE + p0 * 8), 16, 0, 0);
+      for (int i = 0; i < C::VDMA; ++i)
+        __builtin_amdgcn_global_load_lds(base + i * vstep + voff0,
+            (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::VDMA; ++i) {
+        const int p0 = (i * 4 + wave) * 64;
+        const int p = p0 + lane;
+        const int row = p / C::VCPR;
+        const int c = vswz<C::VCPR>(p % C::VCPR, row);
+        const int64_t key = min(key0 + row, last_key);
+        __builtin_amdgcn_global_load_lds(vbase + key * row_elems_v + c * 8,
+            (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, 0, 0);
+      }
     }
   };
 
