@@ -115,6 +115,7 @@ __device__ __forceinline__ int vswz(int c, int r) {
 // waves per SIMD even when a launch has only one workgroup per CU.
 template <int DQK, int DV, int SPLIT>
 __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(StepArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   using C = Bf16Cfg<DQK, DV>;
   // K stages of both halves, then V stages of both halves.
   __shared__ __attribute__((aligned(16))) uint16_t smem[SPLIT * 2 * (C::KTILE + C::VTILE)];
@@ -181,7 +182,6 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   float l_run = 0.f;      // running sum over this lane's half of the keys
 
   const int64_t kv_base = static_cast<int64_t>(b) * a.sk;
-  const int64_t last_key = a.sk - 1;
 
   // Direct global->LDS loads: wave-instruction i of this wave fills 64
   // consecutive 16-byte chunk slots; each lane fetches the logical chunk that
@@ -191,64 +191,51 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
   const uint16_t* kbase = kg + kv_base * row_elems_k + kvh * DQK;
   const uint16_t* vbase = vg + kv_base * row_elems_v + kvh * DV;
-  // Per-lane element offset of this lane's first direct load inside a tile
-  // (loop-invariant).  With 8 or 16 chunks per row, instruction i lands
-  // 256/CPR rows further down and the swizzle (which reads only the low row
-  // bits) is unchanged, so instruction i adds a uniform number of rows.
-  uint32_t koff0 = 0, voff0 = 0;
-  {
-    const int p = wave * 64 + lane;
-    const int kr = p / C::KCPR;
-    koff0 = static_cast<uint32_t>(kr * row_elems_k + kswz<C::KCPR>(p % C::KCPR, kr) * 8);
-    const int vr = p / C::VCPR;
-    voff0 = static_cast<uint32_t>(vr * row_elems_v + vswz<C::VCPR>(p % C::VCPR, vr) * 8);
+  // Direct buffer->LDS loads.  Per tile one buffer descriptor covers the
+  // tile's rows of this (batch, kv head); rows past the end of the block lie
+  // beyond its record count and read as zeros (their scores are masked), so
+  // no tile needs a separate tail path.  Wave-instruction i fills 64
+  // consecutive 16-byte LDS slots; each lane fetches the logical chunk the
+  // swizzle maps to its slot.  Byte offsets inside a tile are loop-invariant.
+  uint32_t koffb[C::KDMA], voffb[C::VDMA];
+#pragma unroll
+  for (int i = 0; i < C::KDMA; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int row = p / C::KCPR;
+    koffb[i] = static_cast<uint32_t>((row * row_elems_k + kswz<C::KCPR>(p % C::KCPR, row) * 8) * 2);
   }
-  constexpr bool kUniformStep = C::KCPR == 8 || C::KCPR == 16;
-  const int64_t kstep = C::KROWS_PER_DMA * row_elems_k;   // elements between direct loads
-  const int64_t vstep = C::VROWS_PER_DMA * row_elems_v;
+#pragma unroll
+  for (int i = 0; i < C::VDMA; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int row = p / C::VCPR;
+    voffb[i] = static_cast<uint32_t>((row * row_elems_v + vswz<C::VCPR>(p % C::VCPR, row) * 8) * 2);
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int64_t key0, int64_t row_elems, int width) {
+    // bytes from the tile start to the end of key sk-1's row of this head
+    const int64_t valid = ((a.sk - 1 - key0) * row_elems + width) * 2;
+    const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
+                                             static_cast<short>(0), nrec, 0x00020000);
+  };
   auto dma_k = [&](int t, int stage) {
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
+    const auto rsrc = tile_rsrc(kbase, key0, row_elems_k, DQK);
     uint16_t* dst = Kh + stage * C::KTILE;
-    if (kUniformStep && key0 + kBN <= a.sk) {
-      const uint16_t* base = kbase + key0 * row_elems_k;
 #pragma unroll
-      for (int i = 0; i < C::KDMA; ++i)
-        __builtin_amdgcn_global_load_lds(base + i * kstep + koff0,
-            (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::KDMA; ++i) {
-        const int p0 = (i * 4 + wave) * 64;
-        const int p = p0 + lane;
-        const int row = p / C::KCPR;
-        const int c = kswz<C::KCPR>(p % C::KCPR, row);
-        const int64_t key = min(key0 + row, last_key);
-        __builtin_amdgcn_global_load_lds(kbase + key * row_elems_k + c * 8,
-            (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, 0, 0);
-      }
-    }
+    for (int i = 0; i < C::KDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          static_cast<int>(koffb[i]), 0, 0, 0);
   };
   auto dma_v = [&](int t, int stage) {
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
+    const auto rsrc = tile_rsrc(vbase, key0, row_elems_v, DV);
     uint16_t* dst = Vh + stage * C::VTILE;
-    if (key0 + kBN <= a.sk) {
-      const uint16_t* base = vbase + key0 * row_elems_v;
 #pragma unroll
-      for (int i = 0; i < C::VDMA; ++i)
-        __builtin_amdgcn_global_load_lds(base + i * vstep + voff0,
-            (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::VDMA; ++i) {
-        const int p0 = (i * 4 + wave) * 64;
-        const int p = p0 + lane;
-        const int row = p / C::VCPR;
-        const int c = vswz<C::VCPR>(p % C::VCPR, row);
-        const int64_t key = min(key0 + row, last_key);
-        __builtin_amdgcn_global_load_lds(vbase + key * row_elems_v + c * 8,
-            (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, 0, 0);
-      }
-    }
+    for (int i = 0; i < C::VDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          static_cast<int>(voffb[i]), 0, 0, 0);
   };
 
   // One K fragment (A operand of S^T = K Q^T): key 32kb + col, d chunk 2c + hh.
@@ -333,10 +320,54 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   const int my_n = ntiles > half ? (ntiles - half + SPLIT - 1) / SPLIT : 0;
   const int n_iter = (ntiles + SPLIT - 1) / SPLIT;
   auto tile = [&](int j) { return j * SPLIT + half; };
+  // Online softmax of tile j (exp2 domain) plus, when there is a next tile,
+  // its scores on MFMA interleaved with the exponentials.  Both halves of a
+  // row share m_run.  It is raised only when some row of the wave gained more
+  // than tau (log2 units); otherwise the stale max stays, which is exact
+  // because numerator and denominator share it, and P stays below 2^tau.
+  auto softmax_and_next_scores = [&](int j, f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, int next_stage) {
+    mask_tile(tile(j), s_cur);
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+    if (__ballot((mx - m_run) * a.scale_log2 > kTau) != 0) {   // false for -inf - -inf
+      const float full = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, full);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
+    if (j + 1 < my_n) {
+      qk(next_stage, s_nxt);               // MFMA: scores of tile j+1 ...
+      l_run += exps(s_cur, pb, neg_mc);    // ... interleaved with the VALU exponentials of tile j
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * C::QC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
+        if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      l_run += exps(s_cur, pb, neg_mc);
+    }
+  };
+
   if (n_iter > 0) {
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 pb[4];
-    // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight; scores of tile 0
+    // Iteration j: [scores of tile j+1 on MFMA + softmax of tile j] then
+    // [P_j V_j].  (Running the two key-split halves in opposite phase orders
+    // was measured slower on gfx950 than this lock-step order.)
+    // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight;
+    // scores of tile 0
     if (my_n > 0) dma_k(tile(0), 0);
     if (my_n > 1) dma_k(tile(1), 1);
     if (my_n > 0) dma_v(tile(0), 0);
@@ -344,56 +375,18 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
     __syncthreads();
     if (my_n > 0) qk(0, s_cur);
     for (int j = 0; j < n_iter; ++j) {
-      // K_{j+1} and V_j have landed for every wave, and every wave is done
-      // with iteration j-1: K stage j%2 (held K_j) and V stage (j+1)%2 (held
-      // V_{j-1}) may be refilled.
+      // The loads issued at the start of iteration j-1 have landed for every
+      // wave, and every wave is done with iteration j-1.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);
-      if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);
+      if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);        // K stage j%2 held K_j (read in j-1)
+      if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);  // V stage (j+1)%2 held V_{j-1}
       if (j < my_n) {
-        mask_tile(tile(j), s_cur);
-
-        // Online softmax, exp2 domain.  Both halves of a row share m_run.  It
-        // is raised only when some row of the wave gained more than tau (log2
-        // units); otherwise the stale max stays, which is exact because
-        // numerator and denominator share it, and P stays below 2^tau.
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
-        if (__ballot((mx - m_run) * a.scale_log2 > kTau) != 0) {   // false for -inf - -inf
-          const float full = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float m_new = fmaxf(m_run, full);
-          const float m_use = m_new == kNegInf ? 0.f : m_new;
-          const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 when m_run = -inf
-          l_run *= alpha;
-#pragma unroll
-          for (int d = 0; d < C::DB; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-          m_run = m_new;
-        }
-        const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
-        if (j + 1 < my_n) {
-          // MFMA: scores of tile j+1, interleaved with the VALU exponentials of tile j
-          qk((j + 1) & 1, s_nxt);
-          l_run += exps(s_cur, pb, neg_mc);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-          for (int i = 0; i < 2 * C::QC; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
-            if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        } else {
-          l_run += exps(s_cur, pb, neg_mc);
-        }
-        pv(j & 1, pb);                        // MFMA: O += P_j V_j
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+        softmax_and_next_scores(j, s_cur, s_nxt, pb, (j + 1) & 1);
+        pv(j & 1, pb);                                     // MFMA: O += P_j V_j
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
   }
 
@@ -454,6 +447,7 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
       *reinterpret_cast<f32x4*>(op + dv0) = val;
     }
   if (hh == 0) a.lse[orow] = lse_out;
+#endif
 }
 
 // ---------------------------------------------------------------------------
