@@ -8,8 +8,8 @@
 // With M = max_k LSE_k:  LSE = M + ln sum_k exp(LSE_k - M),
 //                        O   = sum_k exp(LSE_k - LSE) * O_k.
 //
-// HBM-bound: every thread owns 4 consecutive floats of one row; a row's
-// threads are adjacent, so each part is read with fully coalesced 16-B loads.
+// HBM-bound: every thread owns 16 (or 4) consecutive floats of one row; a
+// row's threads are adjacent, so each part is read with coalesced 16-B loads.
 #include <hip/hip_runtime.h>
 
 #include "kernels_common.h"
@@ -20,44 +20,55 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 
-template <bool OUT_BF16>
+// One pass over the parts with a running maximum (the same online rule the
+// attention kernels use): each thread owns UNROLL x 4 consecutive floats of
+// one row, so UNROLL independent 16-B loads per part are in flight.
+template <bool OUT_BF16, int UNROLL>
 __global__ void __launch_bounds__(kMergeThreads)
 lse_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
                  int32_t n, int64_t rows, int32_t dv, void* __restrict__ o_out,
                  float* __restrict__ lse_out) {
-  const int tpr = dv / 4;  // threads per row
+  const int tpr = dv / (4 * UNROLL);  // threads per row
   const int rpb = kMergeThreads / tpr;
   const int local_row = threadIdx.x / tpr;
-  const int c4 = threadIdx.x % tpr;
+  const int c = threadIdx.x % tpr;
   if (local_row >= rpb) return;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * rpb + local_row;
   if (row >= rows) return;
 
-  float m = kNegInf;
-  for (int k = 0; k < n; ++k) m = fmaxf(m, lse_parts[k * rows + row]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lse = kNegInf;
-  if (m != kNegInf) {
-    float tot = 0.f;
-    for (int k = 0; k < n; ++k) tot += fast_exp2((lse_parts[k * rows + row] - m) * kLog2e);
-    const float inv = 1.f / tot;
-    for (int k = 0; k < n; ++k) {
-      const float w = fast_exp2((lse_parts[k * rows + row] - m) * kLog2e) * inv;
-      if (w != 0.f) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(o_parts + (k * rows + row) * dv + 4 * c4);
-        acc += x * w;
-      }
+  f32x4 acc[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, tot = 0.f;
+  for (int k = 0; k < n; ++k) {
+    const float l = lse_parts[k * rows + row];
+    const float* src = o_parts + (k * rows + row) * dv + 4 * UNROLL * c;
+    f32x4 x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
+    if (l == kNegInf) continue;                 // an empty part changes nothing
+    const float m_new = fmaxf(m, l);
+    const float keep = fast_exp2((m - m_new) * kLog2e);   // 0 while m = -inf
+    const float w = fast_exp2((l - m_new) * kLog2e);
+    tot = tot * keep + w;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc[u] = acc[u] * keep + x[u] * w;
+    m = m_new;
+  }
+  const float inv = m == kNegInf ? 0.f : 1.f / tot;
+  const float lse = m == kNegInf ? kNegInf : m + fast_log2(tot) * kLn2;
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const f32x4 r = acc[u] * inv;
+    if (OUT_BF16) {
+      bf16x4 b = {static_cast<__bf16>(r[0]), static_cast<__bf16>(r[1]), static_cast<__bf16>(r[2]),
+                  static_cast<__bf16>(r[3])};
+      *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(o_out) + row * dv + 4 * UNROLL * c + 4 * u) = b;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + row * dv + 4 * UNROLL * c + 4 * u) = r;
     }
-    lse = m + fast_log2(tot) * kLn2;
   }
-  if (OUT_BF16) {
-    bf16x4 b = {static_cast<__bf16>(acc[0]), static_cast<__bf16>(acc[1]),
-                static_cast<__bf16>(acc[2]), static_cast<__bf16>(acc[3])};
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(o_out) + row * dv + 4 * c4) = b;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + row * dv + 4 * c4) = acc;
-  }
-  if (lse_out != nullptr && c4 == 0) lse_out[row] = lse;
+  if (lse_out != nullptr && c == 0) lse_out[row] = lse;
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -68,19 +79,28 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 int32_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_t n_parts,
                          int64_t rows, int32_t d_v, void* o_out, int32_t out_dtype,
                          float* lse_out, hipStream_t stream) {
-  const int tpr = d_v / 4;
+  const bool wide = d_v % 16 == 0;
+  const int tpr = d_v / (wide ? 16 : 4);
   const int rpb = kMergeThreads / tpr;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   RA_CHECK(blocks < (int64_t{1} << 31), CP_EUNSUPPORTED, "lse_merge: %lld rows too many",
            static_cast<long long>(rows));
-  if (out_dtype == CP_BF16)
-    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kMergeThreads), 0, stream, o_parts, lse_parts, n_parts, rows, d_v,
-                       o_out, lse_out);
-  else
-    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kMergeThreads), 0, stream, o_parts, lse_parts, n_parts, rows, d_v,
-                       o_out, lse_out);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kMergeThreads);
+  if (out_dtype == CP_BF16) {
+    if (wide)
+      hipLaunchKernelGGL((lse_merge_kernel<true, 4>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, rows, d_v, o_out, lse_out);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<true, 1>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, rows, d_v, o_out, lse_out);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((lse_merge_kernel<false, 4>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, rows, d_v, o_out, lse_out);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<false, 1>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, rows, d_v, o_out, lse_out);
+  }
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "lse_merge: launch failed: %s", hipGetErrorString(err));
   return CP_OK;

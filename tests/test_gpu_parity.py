@@ -111,7 +111,8 @@ def test_deterministic(ra):
 
 @pytest.mark.parametrize("n,rows,dv,out_bf16", [(1, 37, 64, False), (4, 512, 64, False),
                                                 (8, 4096, 128, False), (3, 1000, 128, True),
-                                                (2, 65, 192, False)])
+                                                (2, 65, 192, False), (3, 100, 36, False),
+                                                (5, 77, 12, True)])
 def test_lse_merge(ra, n, rows, dv, out_bf16):
     say(f"lse_merge n={n} rows={rows} dv={dv} bf16={out_bf16}")
     r = np.random.default_rng(n * 1000 + rows)
