@@ -161,6 +161,45 @@ int32_t ring_attn_step(const void* q, const void* k, const void* v, int32_t dtyp
                        float* o, float* lse, int32_t* class_out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ring_attn_step_jobs -- one ring step for several local query chunks at once.
+ * [RA] ring-topology excerpt (each step, the device's query chunks meet the
+ * K/V block it holds) and memory-wall excerpt (one running max and sum per
+ * row); [CP] head-tail partition (a device holds two query parts and a K/V
+ * block carries two parts, each with its own positions).
+ *
+ * Each job is one query chunk q [batch, sq, hq, d_qk] at absolute positions
+ * q_pos0.. with its outputs o [batch, sq, hq, d_v] / lse [batch, sq, hq]
+ * (float32).  It attends to the union of its segments' keys; segment s is
+ * k/v [batch, sk_s, hkv, d] at positions k_pos0_s..  With accumulate == 0
+ * the job's (o, lse) are overwritten with that attention (O = 0, LSE = -inf
+ * where no key is visible); with accumulate == 1 it is LSE-merged into them.
+ * Masking, GQA mapping and scale are as for ring_attn_step.  All jobs run
+ * in one launch: they share sq and must write disjoint o / lse buffers
+ * (CP_EINVAL otherwise).  1 <= n_jobs <= 4, 0 <= n_segments <= 4, bf16
+ * only.  Segments that no query can see are skipped on the host.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void* k;   /* [batch, sk, hkv, d_qk] */
+  const void* v;   /* [batch, sk, hkv, d_v]  */
+  int64_t sk;
+  int64_t k_pos0;
+} cp_kv_segment_t;
+
+typedef struct {
+  const void* q;   /* [batch, sq, hq, d_qk] */
+  float* o;        /* [batch, sq, hq, d_v]  */
+  float* lse;      /* [batch, sq, hq]       */
+  int64_t q_pos0;
+  int32_t accumulate;
+  int32_t n_segments;
+  cp_kv_segment_t segments[4];
+} cp_attn_job_t;
+
+int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs, int32_t dtype,
+                            int32_t batch, int64_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
+                            int32_t d_v, int32_t mask, float scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * lse_merge -- combine n partial (O, LSE) results of the same rows.
  * [CP] DCP section (output and LSE combined to update the result);
  * [RA] memory-wall excerpt (running max and running sum).

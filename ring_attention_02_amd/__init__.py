@@ -26,7 +26,8 @@ ABI_VERSION = 1
 # Every symbol include/ringattn.h declares.
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
-            "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy")
+            "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
+            "ring_attn_step_jobs")
 
 
 class RingAttnError(RuntimeError):
@@ -66,6 +67,23 @@ _lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i3
                                  _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.ring_stage_copy.restype = _i32
 _lib.ring_stage_copy.argtypes = [_vp, _vp, _vp, _i32, _vp]
+
+
+class _KvSegment(ctypes.Structure):          # cp_kv_segment_t
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("sk", ctypes.c_int64),
+                ("k_pos0", ctypes.c_int64)]
+
+
+class _AttnJob(ctypes.Structure):            # cp_attn_job_t
+    _fields_ = [("q", ctypes.c_void_p), ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("q_pos0", ctypes.c_int64), ("accumulate", ctypes.c_int32),
+                ("n_segments", ctypes.c_int32), ("segments", _KvSegment * 4)]
+
+
+_lib.ring_attn_step_jobs.restype = _i32
+_lib.ring_attn_step_jobs.argtypes = [_vp, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
+                                     _f32, _vp]
+MAX_JOBS, MAX_SEGMENTS = 4, 4
 
 if _lib.cp_abi_version() != ABI_VERSION:
     raise ImportError(f"libringattn ABI {_lib.cp_abi_version()} != binding ABI {ABI_VERSION}")
@@ -190,6 +208,55 @@ def ring_attn_step(q, k, v, o, lse, q_pos0=0, k_pos0=0, causal=True, scale=None,
     return cls.value
 
 
+def ring_attn_step_jobs(jobs, causal=True, scale=None, stream=None):
+    """One launch for up to 4 query chunks, each over up to 4 K/V segments.
+
+    jobs: list of dicts with q [B,Sq,Hq,Dqk] (bf16), o [B,Sq,Hq,Dv] / lse [B,Sq,Hq]
+    (float32), q_pos0, accumulate, and segments = [(k, v, k_pos0), ...] with
+    k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv].  Every job's result is attention over
+    the union of its segments' keys, written to (or LSE-merged into) o / lse.
+    """
+    torch = _torch()
+    if not 1 <= len(jobs) <= MAX_JOBS:
+        raise ValueError(f"ring_attn_step_jobs takes 1..{MAX_JOBS} jobs")
+    q0 = jobs[0]["q"]
+    B, Sq, Hq, Dqk = q0.shape
+    Hkv, Dv = None, jobs[0]["o"].shape[3]
+    arr = (_AttnJob * len(jobs))()
+    for i, jb in enumerate(jobs):
+        q, o, lse = jb["q"], jb["o"], jb["lse"]
+        if tuple(q.shape) != (B, Sq, Hq, Dqk) or q.dtype != torch.bfloat16:
+            raise ValueError("all jobs need bf16 q of one shape [B, Sq, Hq, Dqk]")
+        if tuple(o.shape) != (B, Sq, Hq, Dv) or o.dtype != torch.float32:
+            raise ValueError("o must be float32 [B, Sq, Hq, Dv]")
+        if tuple(lse.shape) != (B, Sq, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, Sq, Hq]")
+        segs = jb.get("segments", [])
+        if len(segs) > MAX_SEGMENTS:
+            raise ValueError(f"at most {MAX_SEGMENTS} segments per job")
+        arr[i].q, arr[i].o, arr[i].lse = (_dev_ptr(q, "q").value, _dev_ptr(o, "o").value,
+                                          _dev_ptr(lse, "lse").value)
+        arr[i].q_pos0 = int(jb.get("q_pos0", 0))
+        arr[i].accumulate = 1 if jb.get("accumulate", False) else 0
+        arr[i].n_segments = len(segs)
+        for j, (k, v, k_pos0) in enumerate(segs):
+            if k.shape[0] != B or k.shape[3] != Dqk or tuple(v.shape[:3]) != tuple(k.shape[:3]) \
+                    or v.shape[3] != Dv or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+                raise ValueError("segment k/v shapes or dtypes do not agree with q / o")
+            Hkv = k.shape[2] if Hkv is None else Hkv
+            if k.shape[2] != Hkv:
+                raise ValueError("all segments need the same kv heads")
+            arr[i].segments[j] = _KvSegment(_dev_ptr(k, "k").value, _dev_ptr(v, "v").value,
+                                            k.shape[1], int(k_pos0))
+    if Hkv is None:
+        Hkv = Hq
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    _check(_lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs), CP_BF16, B, Sq,
+                                    Hq, Hkv, Dqk, Dv, CP_MASK_CAUSAL if causal else CP_MASK_NONE,
+                                    float(scale), _stream_handle(stream)), "ring_attn_step_jobs")
+
+
 def lse_merge(o_parts, lse_parts, o_out=None, lse_out=None, out_dtype=None, stream=None):
     """Merge partials o_parts [n, ..., Dv] / lse_parts [n, ...]; returns (o, lse)."""
     torch = _torch()
@@ -266,7 +333,8 @@ def stage_copy(pairs, stream=None):
 
 from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E402
 
-__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "lse_merge", "stage_copy",
+__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "ring_attn_step_jobs",
+           "lse_merge", "stage_copy",
            "split_kv_decode", "split_kv_decode_workspace", "ZigzagRing", "segmented_prefill",
            "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
            "last_error"]

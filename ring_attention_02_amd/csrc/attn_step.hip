@@ -51,6 +51,34 @@ struct StepArgs {
   float scale_log2;  // scale * log2(e)
 };
 
+// A ring step of the bf16 kernel: up to kMaxJobs query chunks (same length
+// sq), each attending to up to kMaxSegs K/V segments with their own absolute
+// positions.  A job's segments are swept in order with one online softmax,
+// so its result is attention over the union of their keys.
+constexpr int kMaxJobs = 4;
+constexpr int kMaxSegs = 4;
+struct KvSeg {
+  const void* k;
+  const void* v;
+  int64_t sk, k_pos0;
+};
+struct QJob {
+  const void* q;
+  float* o;
+  float* lse;
+  int64_t q_pos0;
+  int32_t accumulate, n_seg;
+  KvSeg seg[kMaxSegs];
+};
+struct JobArgs {
+  QJob job[kMaxJobs];
+  int64_t sq;
+  int32_t n_jobs, hq, hkv, group;
+  int32_t n_qtiles, total_wgs;
+  int32_t causal, reverse_q;
+  float scale, scale_log2;
+};
+
 // Folds a block partial (o_blk, lse_blk) into the running (o, lse) of one
 // row.  Returns the merged LSE and the weights of the old and the new part.
 __device__ __forceinline__ float merge_weights(float lse_old, float lse_blk, float* w_old,
@@ -114,7 +142,7 @@ __device__ __forceinline__ int vswz(int c, int r) {
 // the two softmax states are merged through LDS at the end.  This keeps two
 // waves per SIMD even when a launch has only one workgroup per CU.
 template <int DQK, int DV, int SPLIT>
-__global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(StepArgs a) {
+__global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(JobArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   using C = Bf16Cfg<DQK, DV>;
   // K stages of both halves, then V stages of both halves.
@@ -134,32 +162,76 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   const int g = lane >> 4;    // 16-lane group (transposed V reads)
   const int i16 = lane & 15;
 
+  // Workgroup -> (job, query tile, head, batch), job fastest so every XCD's
+  // contiguous range mixes all jobs and tile weights.
   const int logical = xcd_contiguous_id(blockIdx.x, a.total_wgs);
-  int qt = logical % a.n_qtiles;
-  const int rest = logical / a.n_qtiles;
+  const int jb = logical % a.n_jobs;
+  int rest = logical / a.n_jobs;
+  int qt = rest % a.n_qtiles;
+  rest /= a.n_qtiles;
   const int h = rest % a.hq;
   const int b = rest / a.hq;
   if (a.reverse_q) qt = a.n_qtiles - 1 - qt;
   const int kvh = h / a.group;
+  const QJob& job = a.job[jb];
 
-  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(job.q);
 
   const int64_t q_first = static_cast<int64_t>(qt) * kBM;
   const int64_t q_last = min(a.sq, q_first + kBM) - 1;  // last valid local row of the WG
   const int64_t wq0 = q_first + wave * 32;              // first row of this wave
   const int64_t my_row = wq0 + col;
   const bool row_valid = my_row < a.sq;
-  const int64_t qpos = a.q_pos0 + my_row;
+  const int64_t qpos = job.q_pos0 + my_row;
 
-  // Keys any row of this workgroup can see.
-  int64_t nkeys = a.sk;
-  if (a.causal) {
-    const int64_t lim = a.q_pos0 + q_last - a.k_pos0 + 1;
-    nkeys = lim < 0 ? 0 : (lim < a.sk ? lim : a.sk);
-  }
-  const int ntiles = static_cast<int>((nkeys + kBN - 1) / kBN);
+  // The job's segments, each with the number of its tiles that some row of
+  // this workgroup can see; the sweep walks them segment after segment
+  // ("virtual" tile numbers).  Everything here is uniform over the workgroup
+  // and kept in named scalars: a per-lane array would be indexed per lane.
+  struct Seg {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t sk, k_pos0;
+    int tiles;
+  };
+  auto load_seg = [&](int sg) -> Seg {
+    Seg r{nullptr, nullptr, 0, 0, 0};
+    if (sg < job.n_seg) {
+      const KvSeg& x = job.seg[sg];
+      r.k = static_cast<const uint16_t*>(x.k);
+      r.v = static_cast<const uint16_t*>(x.v);
+      r.sk = x.sk;
+      r.k_pos0 = x.k_pos0;
+      int64_t nkeys = x.sk;
+      if (a.causal) {
+        const int64_t lim = job.q_pos0 + q_last - x.k_pos0 + 1;
+        nkeys = lim < 0 ? 0 : (lim < nkeys ? lim : nkeys);
+      }
+      r.tiles = static_cast<int>((nkeys + kBN - 1) / kBN);
+    }
+    return r;
+  };
+  static_assert(kMaxSegs == 4, "segment selection below is written for four segments");
+  const Seg seg0 = load_seg(0), seg1 = load_seg(1), seg2 = load_seg(2), seg3 = load_seg(3);
+  const int ntiles = seg0.tiles + seg1.tiles + seg2.tiles + seg3.tiles;
+  // virtual tile vt -> its segment, and the tile within it in *t
+  auto locate = [&](int vt, int* t) -> Seg {
+    Seg r = seg0;
+    if (vt >= seg0.tiles) {
+      vt -= seg0.tiles;
+      r = seg1;
+      if (vt >= seg1.tiles) {
+        vt -= seg1.tiles;
+        r = seg2;
+        if (vt >= seg2.tiles) {
+          vt -= seg2.tiles;
+          r = seg3;
+        }
+      }
+    }
+    *t = vt;
+    return r;
+  };
 
   // Q^T fragment (B operand): for step c the lane holds Q[row][16c + 8hh .. +7].
   bf16x8 qf[C::QC];
@@ -181,22 +253,14 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   float m_run = kNegInf;  // running max of raw scores of this lane's row (possibly stale by < tau)
   float l_run = 0.f;      // running sum over this lane's half of the keys
 
-  const int64_t kv_base = static_cast<int64_t>(b) * a.sk;
-
-  // Direct global->LDS loads: wave-instruction i of this wave fills 64
-  // consecutive 16-byte chunk slots; each lane fetches the logical chunk that
-  // the swizzle maps to its slot.  Rows past the end of the block re-read the
-  // last key (finite values; their scores are masked).
-  const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
-  const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
-  const uint16_t* kbase = kg + kv_base * row_elems_k + kvh * DQK;
-  const uint16_t* vbase = vg + kv_base * row_elems_v + kvh * DV;
   // Direct buffer->LDS loads.  Per tile one buffer descriptor covers the
-  // tile's rows of this (batch, kv head); rows past the end of the block lie
+  // tile's rows of this (batch, kv head); rows past the end of the segment lie
   // beyond its record count and read as zeros (their scores are masked), so
   // no tile needs a separate tail path.  Wave-instruction i fills 64
   // consecutive 16-byte LDS slots; each lane fetches the logical chunk the
   // swizzle maps to its slot.  Byte offsets inside a tile are loop-invariant.
+  const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
+  const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
   uint32_t koffb[C::KDMA], voffb[C::VDMA];
 #pragma unroll
   for (int i = 0; i < C::KDMA; ++i) {
@@ -210,16 +274,22 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
     const int row = p / C::VCPR;
     voffb[i] = static_cast<uint32_t>((row * row_elems_v + vswz<C::VCPR>(p % C::VCPR, row) * 8) * 2);
   }
-  auto tile_rsrc = [&](const uint16_t* base, int64_t key0, int64_t row_elems, int width) {
+  // Descriptor of tile t of segment sgm for K (is_k) or V.
+  auto tile_rsrc = [&](const Seg& sgm, int t, bool is_k) {
+    const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
+    const int width = is_k ? DQK : DV;
+    const uint16_t* base = (is_k ? sgm.k : sgm.v) + (static_cast<int64_t>(b) * sgm.sk * a.hkv + kvh) * width;
+    const int64_t key0 = static_cast<int64_t>(t) * kBN;
     // bytes from the tile start to the end of key sk-1's row of this head
-    const int64_t valid = ((a.sk - 1 - key0) * row_elems + width) * 2;
+    const int64_t valid = ((sgm.sk - 1 - key0) * row_elems + width) * 2;
     const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
                                              static_cast<short>(0), nrec, 0x00020000);
   };
-  auto dma_k = [&](int t, int stage) {
-    const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const auto rsrc = tile_rsrc(kbase, key0, row_elems_k, DQK);
+  auto dma_k = [&](int vt, int stage) {
+    int t;
+    const Seg sgm = locate(vt, &t);
+    const auto rsrc = tile_rsrc(sgm, t, true);
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::KDMA; ++i)
@@ -227,9 +297,10 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
           rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
           static_cast<int>(koffb[i]), 0, 0, 0);
   };
-  auto dma_v = [&](int t, int stage) {
-    const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const auto rsrc = tile_rsrc(vbase, key0, row_elems_v, DV);
+  auto dma_v = [&](int vt, int stage) {
+    int t;
+    const Seg sgm = locate(vt, &t);
+    const auto rsrc = tile_rsrc(sgm, t, false);
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
     for (int i = 0; i < C::VDMA; ++i)
@@ -283,13 +354,15 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
       if (i + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
-  auto mask_tile = [&](int t, f32x16* s) {
+  auto mask_tile = [&](int vt, f32x16* s) {
+    int t;
+    const Seg sgm = locate(vt, &t);
+    const int64_t sk = sgm.sk, k_pos0 = sgm.k_pos0;
     const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const bool need = (key0 + kBN > a.sk) ||
-                      (a.causal && a.k_pos0 + key0 + kBN - 1 > a.q_pos0 + wq0);
+    const bool need = (key0 + kBN > sk) || (a.causal && k_pos0 + key0 + kBN - 1 > job.q_pos0 + wq0);
     if (!need) return;
     // visible iff local key < min(sk, qpos - k_pos0 + 1)
-    const int64_t lim64 = a.causal ? min(a.sk, qpos - a.k_pos0 + 1) : a.sk;
+    const int64_t lim64 = a.causal ? min(sk, qpos - k_pos0 + 1) : sk;
     const int lim = static_cast<int>(max(min(lim64 - key0, static_cast<int64_t>(kBN)), static_cast<int64_t>(0)));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -429,9 +502,9 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
   const float inv = has ? 1.f / l_tot : 0.f;
   const float lse_blk = has ? m_run * a.scale + fast_log2(l_tot) * kLn2 : kNegInf;
   const int64_t orow = (static_cast<int64_t>(b) * a.sq + my_row) * a.hq + h;
-  float* op = a.o + orow * DV;
+  float* op = job.o + orow * DV;
   float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
-  if (a.accumulate) lse_out = merge_weights(a.lse[orow], lse_blk, &w_old, &w_blk);
+  if (job.accumulate) lse_out = merge_weights(job.lse[orow], lse_blk, &w_old, &w_blk);
   const float wb = w_blk * inv;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
@@ -440,13 +513,13 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Ste
       const int dv0 = d * 32 + 8 * j + 4 * hh;
       f32x4 val = {oacc[d][4 * j] * wb, oacc[d][4 * j + 1] * wb, oacc[d][4 * j + 2] * wb,
                    oacc[d][4 * j + 3] * wb};
-      if (a.accumulate) {
+      if (job.accumulate) {
         const f32x4 old = *reinterpret_cast<const f32x4*>(op + dv0);
         val += old * w_old;
       }
       *reinterpret_cast<f32x4*>(op + dv0) = val;
     }
-  if (hh == 0) a.lse[orow] = lse_out;
+  if (hh == 0) job.lse[orow] = lse_out;
 #endif
 }
 
@@ -605,13 +678,36 @@ int device_cus() {
 // bf16 launch: a grid with fewer than two 4-wave workgroups per CU runs the
 // 8-wave key-split variant so every SIMD still holds two waves.
 template <int DQK, int DV>
-int32_t launch_bf16(StepArgs args, int64_t batch, hipStream_t stream) {
-  const int64_t wgs = (args.sq + kBM - 1) / kBM * args.hq * batch;
+int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
+  const int64_t n_qtiles = (args.sq + kBM - 1) / kBM;
+  const int64_t total = n_qtiles * args.n_jobs * args.hq * batch;
+  RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
+           "ring_attn_step: %lld workgroups exceed the grid limit", static_cast<long long>(total));
+  args.n_qtiles = static_cast<int32_t>(n_qtiles);
+  args.total_wgs = static_cast<int32_t>(total);
+  const dim3 grid(static_cast<unsigned>(total));
   if constexpr (DQK <= 128) {
-    if (wgs < 2 * static_cast<int64_t>(device_cus()))
-      return launch(attn_step_bf16_kernel<DQK, DV, 2>, kBM, 2 * kThreads, args, batch, stream);
+    if (total < 2 * static_cast<int64_t>(device_cus())) {
+      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2>), grid, dim3(2 * kThreads), 0, stream, args);
+      const hipError_t err = hipGetLastError();
+      RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
+      return CP_OK;
+    }
   }
-  return launch(attn_step_bf16_kernel<DQK, DV, 1>, kBM, kThreads, args, batch, stream);
+  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1>), grid, dim3(kThreads), 0, stream, args);
+  const hipError_t err = hipGetLastError();
+  RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
+  return CP_OK;
+}
+
+int32_t launch_bf16_any(int32_t d_qk, JobArgs args, int64_t batch, hipStream_t stream) {
+  if (d_qk == 64) return launch_bf16<64, 64>(args, batch, stream);
+  if (d_qk == 128) return launch_bf16<128, 128>(args, batch, stream);
+  return launch_bf16<192, 128>(args, batch, stream);
+}
+
+bool head_dims_ok(int32_t d_qk, int32_t d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -638,9 +734,7 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
            accumulate);
   RA_CHECK(scale > 0.f && scale < __builtin_huge_valf(), CP_EINVAL,
            "ring_attn_step: scale must be positive and finite");
-  const bool pair_ok = (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) ||
-                       (d_qk == 192 && d_v == 128);
-  RA_CHECK(pair_ok, CP_EUNSUPPORTED, "ring_attn_step: (d_qk, d_v) = (%d, %d) not supported", d_qk,
+  RA_CHECK(head_dims_ok(d_qk, d_v), CP_EUNSUPPORTED, "ring_attn_step: (d_qk, d_v) = (%d, %d) not supported", d_qk,
            d_v);
   const int64_t rows = static_cast<int64_t>(batch) * sq * hq;
   const bool work = rows > 0;
@@ -673,12 +767,14 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
       args.scale_log2 = scale * kLog2e;
       int32_t rc;
       if (dtype == CP_BF16) {
-        if (d_qk == 64)
-          rc = launch_bf16<64, 64>(args, batch, st);
-        else if (d_qk == 128)
-          rc = launch_bf16<128, 128>(args, batch, st);
-        else
-          rc = launch_bf16<192, 128>(args, batch, st);
+        JobArgs ja{};
+        ja.job[0].q = q; ja.job[0].o = o; ja.job[0].lse = lse;
+        ja.job[0].q_pos0 = q_pos0; ja.job[0].accumulate = accumulate; ja.job[0].n_seg = 1;
+        ja.job[0].seg[0] = KvSeg{k, v, sk, k_pos0};
+        ja.sq = sq; ja.n_jobs = 1; ja.hq = hq; ja.hkv = hkv; ja.group = hq / hkv;
+        ja.causal = args.causal; ja.reverse_q = args.reverse_q;
+        ja.scale = scale; ja.scale_log2 = args.scale_log2;
+        rc = launch_bf16_any(d_qk, ja, batch, st);
       } else {
         if (d_qk == 64)
           rc = launch(attn_step_f32_kernel<64, 64>, kF32Rows, kF32Rows, args, batch, st);
@@ -692,4 +788,77 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
   }
   if (class_out) *class_out = cls;
   return ok();
+}
+
+extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs, int32_t dtype,
+                                       int32_t batch, int64_t sq, int32_t hq, int32_t hkv,
+                                       int32_t d_qk, int32_t d_v, int32_t mask, float scale,
+                                       void* stream) {
+  RA_CHECK(dtype == CP_BF16 || dtype == CP_F32, CP_EDTYPE, "ring_attn_step_jobs: dtype=%d", dtype);
+  RA_CHECK(dtype == CP_BF16, CP_EUNSUPPORTED, "ring_attn_step_jobs: only bf16 inputs");
+  RA_CHECK(jobs != nullptr && n_jobs >= 1 && n_jobs <= kMaxJobs, CP_EINVAL,
+           "ring_attn_step_jobs: n_jobs=%d outside [1, %d]", n_jobs, kMaxJobs);
+  RA_CHECK(batch >= 0 && sq >= 0, CP_EINVAL, "ring_attn_step_jobs: negative size");
+  RA_CHECK(hq > 0 && hkv > 0 && hq % hkv == 0, CP_EINVAL,
+           "ring_attn_step_jobs: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  RA_CHECK(mask == CP_MASK_NONE || mask == CP_MASK_CAUSAL, CP_EINVAL,
+           "ring_attn_step_jobs: mask=%d", mask);
+  RA_CHECK(scale > 0.f && scale < __builtin_huge_valf(), CP_EINVAL,
+           "ring_attn_step_jobs: scale must be positive and finite");
+  RA_CHECK(head_dims_ok(d_qk, d_v), CP_EUNSUPPORTED,
+           "ring_attn_step_jobs: (d_qk, d_v) = (%d, %d) not supported", d_qk, d_v);
+  const int64_t rows = static_cast<int64_t>(batch) * sq * hq;
+  const int64_t o_bytes = rows * d_v * 4, lse_bytes = rows * 4;
+  for (int j = 0; j < n_jobs; ++j) {
+    const cp_attn_job_t& jb = jobs[j];
+    RA_CHECK(jb.accumulate == 0 || jb.accumulate == 1, CP_EINVAL,
+             "ring_attn_step_jobs: job %d accumulate=%d", j, jb.accumulate);
+    RA_CHECK(jb.n_segments >= 0 && jb.n_segments <= kMaxSegs, CP_EINVAL,
+             "ring_attn_step_jobs: job %d has %d segments (at most %d)", j, jb.n_segments, kMaxSegs);
+    if (rows == 0) continue;
+    RA_CHECK(jb.q && jb.o && jb.lse && aligned16(jb.q) && aligned16(jb.o), CP_EINVAL,
+             "ring_attn_step_jobs: job %d needs 16-byte aligned q/o and a lse pointer", j);
+    for (int sg = 0; sg < jb.n_segments; ++sg) {
+      const cp_kv_segment_t& sgm = jb.segments[sg];
+      RA_CHECK(sgm.sk >= 0, CP_EINVAL, "ring_attn_step_jobs: job %d segment %d sk < 0", j, sg);
+      RA_CHECK(sgm.sk == 0 || (sgm.k && sgm.v && aligned16(sgm.k) && aligned16(sgm.v)), CP_EINVAL,
+               "ring_attn_step_jobs: job %d segment %d needs 16-byte aligned k/v", j, sg);
+    }
+    // concurrent jobs must not write the same output rows
+    for (int i = 0; i < j; ++i) {
+      const auto overlap = [](const void* x, const void* y, int64_t n) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
+        return a0 < b0 + n && b0 < a0 + n;
+      };
+      RA_CHECK(!overlap(jobs[i].o, jb.o, o_bytes) && !overlap(jobs[i].lse, jb.lse, lse_bytes),
+               CP_EINVAL, "ring_attn_step_jobs: jobs %d and %d write overlapping outputs", i, j);
+    }
+  }
+  if (rows == 0) return ok();
+
+  JobArgs ja{};
+  bool any_diag = false, any_work = false;
+  for (int j = 0; j < n_jobs; ++j) {
+    const cp_attn_job_t& jb = jobs[j];
+    QJob& qj = ja.job[j];
+    qj.q = jb.q; qj.o = jb.o; qj.lse = jb.lse; qj.q_pos0 = jb.q_pos0;
+    qj.accumulate = jb.accumulate;
+    int n = 0;
+    for (int sg = 0; sg < jb.n_segments; ++sg) {   // SKIP segments add nothing
+      const cp_kv_segment_t& sgm = jb.segments[sg];
+      const int32_t cls = classify_pair(jb.q_pos0, sq, sgm.k_pos0, sgm.sk, mask);
+      if (cls == CP_CLASS_SKIP) continue;
+      any_diag |= cls == CP_CLASS_DIAG;
+      qj.seg[n++] = KvSeg{sgm.k, sgm.v, sgm.sk, sgm.k_pos0};
+    }
+    qj.n_seg = n;
+    any_work |= n > 0 || !jb.accumulate;   // a job without keys still writes its empty partial
+  }
+  if (!any_work) return ok();
+  ja.sq = sq; ja.n_jobs = n_jobs; ja.hq = hq; ja.hkv = hkv; ja.group = hq / hkv;
+  ja.causal = mask == CP_MASK_CAUSAL;
+  ja.reverse_q = any_diag;   // heaviest query tiles first
+  ja.scale = scale; ja.scale_log2 = scale * kLog2e;
+  const int32_t rc = launch_bf16_any(d_qk, ja, batch, static_cast<hipStream_t>(stream));
+  return rc == CP_OK ? ok() : rc;
 }

@@ -20,7 +20,7 @@ block in place.
 
 import math
 
-from . import ring_attn_step, lse_merge, classify, stage_copy, FULL, DIAG, SKIP
+from . import ring_attn_step, ring_attn_step_jobs, lse_merge, classify, stage_copy, FULL, DIAG, SKIP
 
 
 def _torch():
@@ -103,30 +103,28 @@ class ZigzagRing:
                 ks, vs = self.kbuf[t % 2], self.vbuf[t % 2]
             if 1 <= t and t + 1 < self.cp:
                 self._stage(t + 1)
+            # One launch per ring step: each local Q part is a job over the
+            # block's parts it can see (SKIP parts are left out).
+            jobs, step_cls = [], FULL
             for qi, qp in enumerate(self.q_parts):
                 qs = slice(qi * c, (qi + 1) * c)
-                classes = [classify(qp * c, c, kp * c, c, True) for kp in kv_parts]
-                if t > 0 and classes == [FULL, FULL]:
-                    # Both staged parts are wholly visible and sit side by side
-                    # in the slot: one launch over 2c keys (no mask needed).
-                    groups = [(0, 2, False, FULL)]
+                segs = []
+                for kj, kp in enumerate(kv_parts):
+                    cls = classify(qp * c, c, kp * c, c, True)
+                    if cls != SKIP:
+                        segs.append((ks[kj], vs[kj], kp * c))
+                        step_cls = DIAG if cls == DIAG else step_cls
+                acc = not first[qi]
+                first[qi] = False
+                if segs or not acc:
+                    jobs.append(dict(q=q_local[:, qs], o=o[:, qs], lse=lse[:, qs],
+                                     q_pos0=qp * c, accumulate=acc, segments=segs))
+            if jobs:
+                if on_launch is None:
+                    ring_attn_step_jobs(jobs, causal=True, scale=scale)
                 else:
-                    groups = [(kj, kj + 1, True, classes[kj]) for kj in range(2)]
-                for k0, k1, causal, cls in groups:
-                    acc = not first[qi]
-                    if t > 0:
-                        kk = self.kbuf[t % 2][k0:k1].view(1, (k1 - k0) * c, *ks.shape[3:])
-                        vv = self.vbuf[t % 2][k0:k1].view(1, (k1 - k0) * c, *vs.shape[3:])
-                    else:
-                        kk, vv = ks[k0], vs[k0]
-                    args = (q_local[:, qs], kk, vv, o[:, qs], lse[:, qs])
-                    kw = dict(q_pos0=qp * c, k_pos0=kv_parts[k0] * c, causal=causal,
-                              scale=scale, accumulate=acc)
-                    if on_launch is None:
-                        ring_attn_step(*args, **kw)
-                    else:
-                        on_launch(t, qi, k0, cls, lambda a=args, k=kw: ring_attn_step(*a, **k))
-                    first[qi] = False
+                    on_launch(t, 0, 0, step_cls,
+                              lambda j=jobs: ring_attn_step_jobs(j, causal=True, scale=scale))
             if t >= 1:
                 self.free[t % 2].record(main)
                 self.pending_free[t % 2] = True
@@ -169,15 +167,24 @@ def segmented_prefill(q, k, v, o, lse, q_pos0, segment, k_pos0=0, causal=True, s
     """
     sk = k.shape[1]
     n_seg = max(1, math.ceil(sk / segment))
-    for s in range(n_seg):
-        a, b = s * segment, min(sk, (s + 1) * segment)
-        args = (q, k[:, a:b], v[:, a:b], o, lse)
-        kw = dict(q_pos0=q_pos0, k_pos0=k_pos0 + a, causal=causal, scale=scale, accumulate=s > 0)
+    bounds = [(s_ * segment, min(sk, (s_ + 1) * segment)) for s_ in range(n_seg)]
+    if q.dtype != _torch().bfloat16:
+        # float32: one ring step per segment, each merged into the running result
+        for s_, (a, b) in enumerate(bounds):
+            ring_attn_step(q, k[:, a:b], v[:, a:b], o, lse, q_pos0=q_pos0, k_pos0=k_pos0 + a,
+                           causal=causal, scale=scale, accumulate=s_ > 0)
+        return o, lse
+    # up to four segments per launch; the first launch overwrites o / lse
+    for g in range(0, n_seg, 4):
+        group = bounds[g:g + 4]
+        segs = [(k[:, a:b], v[:, a:b], k_pos0 + a) for a, b in group]
+        job = [dict(q=q, o=o, lse=lse, q_pos0=q_pos0, accumulate=g > 0, segments=segs)]
         if on_launch is None:
-            ring_attn_step(*args, **kw)
+            ring_attn_step_jobs(job, causal=causal, scale=scale)
         else:
-            cls = classify(q_pos0, q.shape[1], k_pos0 + a, b - a, causal)
-            on_launch(s, 0, s, cls, lambda a_=args, k_=kw: ring_attn_step(*a_, **k_))
+            cls = DIAG if any(classify(q_pos0, q.shape[1], k_pos0 + a, b - a, causal) == DIAG
+                              for a, b in group) else FULL
+            on_launch(g, 0, g, cls, lambda j=job: ring_attn_step_jobs(j, causal=causal, scale=scale))
     return o, lse
 
 

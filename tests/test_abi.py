@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 12, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
@@ -175,3 +175,33 @@ def test_stage_copy_validates_before_launch(ra):
     misaligned = (ctypes.c_void_p * n)(256, 520)
     assert lib.ring_stage_copy(misaligned, srcs, good, 2, None) == ra.CP_EINVAL
     assert lib.ring_stage_copy(None, srcs, good, 2, None) == ra.CP_EINVAL
+
+
+def test_jobs_validate_before_launch(ra):
+    import ring_attention_02_amd as m
+    lib = ra.lib()
+
+    def job(q, o, lse, nseg=1, acc=0):
+        j = m._AttnJob()
+        j.q, j.o, j.lse, j.q_pos0, j.accumulate, j.n_segments = q, o, lse, 0, acc, nseg
+        for s in range(4):
+            j.segments[s] = m._KvSegment(4096, 8192, 16, 0)
+        return j
+
+    def call(jobs, dtype=0, dqk=128, dv=128):
+        arr = (m._AttnJob * len(jobs))(*jobs)
+        return lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs), dtype, 1, 16,
+                                       4, 4, dqk, dv, 1, 0.1, None)
+
+    o_bytes = 16 * 4 * 128 * 4
+    a = job(1 << 20, 2 << 20, 3 << 20)
+    b = job(1 << 20, (2 << 20) + o_bytes // 2, 4 << 20)     # overlaps a's output
+    assert call([a, b]) == ra.CP_EINVAL and "overlapping" in ra.last_error()
+    assert call([job(1 << 20, 2 << 20, 3 << 20, nseg=5)]) == ra.CP_EINVAL
+    assert call([job(1 << 20, 2 << 20, 3 << 20, acc=2)]) == ra.CP_EINVAL
+    assert call([a], dtype=1) == ra.CP_EUNSUPPORTED
+    assert call([a], dqk=96, dv=96) == ra.CP_EUNSUPPORTED
+    assert call([job(1 << 20 | 8, 2 << 20, 3 << 20)]) == ra.CP_EINVAL      # misaligned q
+    arr = (m._AttnJob * 5)(*([a] * 5))
+    assert lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), 5, 0, 1, 16, 4, 4, 128, 128,
+                                   1, 0.1, None) == ra.CP_EINVAL

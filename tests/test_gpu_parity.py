@@ -289,3 +289,46 @@ def test_stage_copy_pieces(ra):
     for d, s_ in zip(dst, src):
         assert torch.equal(d, s_)
     assert torch.equal(big_dst[0], big[1]) and torch.equal(big_dst[1], big[0])
+
+
+@pytest.mark.parametrize("dqk,dv,hq,hkv", [(128, 128, 4, 2), (64, 64, 2, 2), (192, 128, 2, 1)])
+def test_jobs_union_of_segments(ra, dqk, dv, hq, hkv):
+    """Several query chunks in one launch, each over scattered K/V segments
+    (one of them invisible, one job with no segment), against the oracle on
+    the union of keys; accumulate on one job."""
+    sq = 200
+    def seg(cfg, sk):
+        k, k64 = tensor(cfg, 2, sk, (1, sk, hkv, dqk), torch.bfloat16)
+        v, v64 = tensor(cfg, 3, sk, (1, sk, hkv, dv), torch.bfloat16)
+        return k, v, k64, v64
+    segs = {n: seg(70 + i, n) for i, n in enumerate((100, 257, 64, 130))}
+    layout = [  # (q_pos0, [(segment size, k_pos0)], accumulate)
+        (1000, [(100, 0), (257, 990), (64, 5000)], False),   # FULL, DIAG, invisible
+        (300, [(130, 250), (64, 0)], True),                   # DIAG, FULL; merged into previous
+        (50, [], False),                                      # no keys: empty partial
+    ]
+    jobs, refs = [], []
+    for i, (q0, sg, acc) in enumerate(layout):
+        q, q64 = tensor(80 + i, 1, 0, (1, sq, hq, dqk), torch.bfloat16)
+        o = torch.full((1, sq, hq, dv), 3.0, device="cuda")
+        lse = torch.full((1, sq, hq), 1.0, device="cuda")
+        kk = [segs[n][2] for n, _ in sg]
+        vv = [segs[n][3] for n, _ in sg]
+        kp = [p0 + np.arange(n) for n, p0 in sg]
+        if acc:   # a previous partial over 40 keys just before the segments
+            k2, k2_64 = tensor(90, 2, 0, (1, 40, hkv, dqk), torch.bfloat16)
+            v2, v2_64 = tensor(90, 3, 0, (1, 40, hkv, dv), torch.bfloat16)
+            ra.ring_attn_step(q, k2, v2, o, lse, q_pos0=q0, k_pos0=200, causal=True)
+            kk, vv, kp = [k2_64] + kk, [v2_64] + vv, [200 + np.arange(40)] + kp
+        jobs.append(dict(q=q, o=o, lse=lse, q_pos0=q0, accumulate=acc,
+                         segments=[(segs[n][0], segs[n][1], p0) for n, p0 in sg]))
+        if kk:
+            ro, rl = oracle.attention_ref(q64, np.concatenate(kk, 1), np.concatenate(vv, 1),
+                                          q0 + np.arange(sq), np.concatenate(kp), True)
+        else:
+            ro, rl = np.zeros((1, sq, hq, dv)), np.full((1, sq, hq), -np.inf)
+        refs.append((o, lse, ro, rl))
+    ra.ring_attn_step_jobs(jobs, causal=True)
+    torch.cuda.synchronize()
+    for i, (o, lse, ro, rl) in enumerate(refs):
+        compare(host64(o), host64(lse), ro, rl, BF16_O, BF16_LSE, f"job {i}")
