@@ -6,9 +6,10 @@
 Prints ONE JSON line.  The headline workload is the zigzag causal ring
 prefill of one rank: seq 8192, cp 4 (8 chunks of 1024), rank 0 holding Q
 chunks {0, 7}, 32 heads, d 128, bf16 with float32 accumulation.  A step is
-one full ring sweep of that rank: 4 ring steps, each staging the next K/V
-block on a side stream while the 4 (Q chunk, K/V chunk) pairs of the current
-block run (7 FULL, 2 DIAG and 7 SKIP pairs overall), merged in place.
+one full ring sweep of that rank: 4 ring steps of one launch each, which
+computes the (Q chunk, K/V chunk) pairs of the current block (7 FULL, 2 DIAG
+and 7 SKIP pairs overall, merged in place) and copies the next K/V block
+into the idle staging slot.
 `value` is algorithmic causal-attention TFLOP/s: visible (q, k) pairs x
 heads x (2 d_qk + 2 d_v) per sweep / time per sweep.
 
@@ -304,7 +305,8 @@ def main():
                    "launches_per_step": l2["launches_per_step"],
                    "full_pair_ms": round(l2["full_ms"], 5), "diag_pair_ms": round(l2["diag_ms"], 5),
                    "timing": "HIP-graph replay of the step's kernels back to back, HIP events"},
-        "launch": {"mode": "HIP graph replay of the whole sweep (copies + kernels)",
+        "launch": {"mode": "HIP graph replay of the whole sweep (one launch per ring "
+                           "step, next block's copy inside it)",
                    "eager_ms_per_step": round(l2["eager_ms"], 4)},
     }
     del w2["ring"]

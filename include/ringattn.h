@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RINGATTN_ABI_VERSION 1
+#define RINGATTN_ABI_VERSION 2
 
 typedef enum {
   CP_OK = 0,
@@ -177,6 +177,19 @@ int32_t ring_attn_step(const void* q, const void* k, const void* v, int32_t dtyp
  * in one launch: they share sq and must write disjoint o / lse buffers
  * (CP_EINVAL otherwise).  1 <= n_jobs <= 4, 0 <= n_segments <= 4, bf16
  * only.  Segments that no query can see are skipped on the host.
+ *
+ * forward / n_forward (0 <= n_forward <= 4; forward may be NULL when 0):
+ * byte ranges the same launch copies src -> dst while it computes -- the
+ * K/V block that moves on around the ring ([RA] ring-topology excerpt: a
+ * device passes its block on while it computes with it; [VID] chapter on
+ * the wire budget: the transfer overlaps the step).  On one GPU the next
+ * step's block is copied into the idle staging slot; the workgroups of the
+ * attention launch each move a slice in their prologue, so no second
+ * stream, event or copy kernel is needed.  dst / src are device pointers,
+ * 16-byte aligned, bytes a multiple of 16.  A dst range may overlap no
+ * other forward range (src or dst) and no q / o / lse / k / v buffer of the
+ * jobs (CP_EINVAL).  The copies complete with the launch (stream order),
+ * also when no job has any visible key.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const void* k;   /* [batch, sk, hkv, d_qk] */
@@ -195,7 +208,14 @@ typedef struct {
   cp_kv_segment_t segments[4];
 } cp_attn_job_t;
 
-int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs, int32_t dtype,
+typedef struct {
+  void* dst;
+  const void* src;
+  int64_t bytes;
+} cp_copy_t;
+
+int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs,
+                            const cp_copy_t* forward, int32_t n_forward, int32_t dtype,
                             int32_t batch, int64_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
                             int32_t d_v, int32_t mask, float scale, void* stream);
 

@@ -21,7 +21,7 @@ CP_OK, CP_EINVAL, CP_EDTYPE, CP_EUNSUPPORTED, CP_EHIP = 0, 1, 2, 3, 4
 CP_BF16, CP_F32 = 0, 1
 CP_MASK_NONE, CP_MASK_CAUSAL = 0, 1
 FULL, DIAG, SKIP = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every symbol include/ringattn.h declares.
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
@@ -80,10 +80,14 @@ class _AttnJob(ctypes.Structure):            # cp_attn_job_t
                 ("n_segments", ctypes.c_int32), ("segments", _KvSegment * 4)]
 
 
+class _Copy(ctypes.Structure):                # cp_copy_t
+    _fields_ = [("dst", ctypes.c_void_p), ("src", ctypes.c_void_p), ("bytes", ctypes.c_int64)]
+
+
 _lib.ring_attn_step_jobs.restype = _i32
-_lib.ring_attn_step_jobs.argtypes = [_vp, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32,
-                                     _f32, _vp]
-MAX_JOBS, MAX_SEGMENTS = 4, 4
+_lib.ring_attn_step_jobs.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                     _i32, _i32, _f32, _vp]
+MAX_JOBS, MAX_SEGMENTS, MAX_FORWARD = 4, 4, 4
 
 if _lib.cp_abi_version() != ABI_VERSION:
     raise ImportError(f"libringattn ABI {_lib.cp_abi_version()} != binding ABI {ABI_VERSION}")
@@ -208,13 +212,16 @@ def ring_attn_step(q, k, v, o, lse, q_pos0=0, k_pos0=0, causal=True, scale=None,
     return cls.value
 
 
-def ring_attn_step_jobs(jobs, causal=True, scale=None, stream=None):
+def ring_attn_step_jobs(jobs, causal=True, scale=None, stream=None, forward=()):
     """One launch for up to 4 query chunks, each over up to 4 K/V segments.
 
     jobs: list of dicts with q [B,Sq,Hq,Dqk] (bf16), o [B,Sq,Hq,Dv] / lse [B,Sq,Hq]
     (float32), q_pos0, accumulate, and segments = [(k, v, k_pos0), ...] with
     k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv].  Every job's result is attention over
     the union of its segments' keys, written to (or LSE-merged into) o / lse.
+    forward: up to 4 (dst, src) pairs of equally sized contiguous GPU tensors
+    that the same launch copies while it computes (the block passed on
+    around the ring); no dst may overlap anything else the launch touches.
     """
     torch = _torch()
     if not 1 <= len(jobs) <= MAX_JOBS:
@@ -252,7 +259,16 @@ def ring_attn_step_jobs(jobs, causal=True, scale=None, stream=None):
         Hkv = Hq
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
-    _check(_lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs), CP_BF16, B, Sq,
+    if len(forward) > MAX_FORWARD:
+        raise ValueError(f"at most {MAX_FORWARD} forwarded ranges")
+    fwd = (_Copy * max(1, len(forward)))()
+    for i, (dst, src) in enumerate(forward):
+        nbytes = dst.numel() * dst.element_size()
+        if nbytes != src.numel() * src.element_size():
+            raise ValueError("forward: dst and src sizes differ")
+        fwd[i] = _Copy(_dev_ptr(dst, "forward dst").value, _dev_ptr(src, "forward src").value, nbytes)
+    _check(_lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs),
+                                    ctypes.cast(fwd, ctypes.c_void_p), len(forward), CP_BF16, B, Sq,
                                     Hq, Hkv, Dqk, Dv, CP_MASK_CAUSAL if causal else CP_MASK_NONE,
                                     float(scale), _stream_handle(stream)), "ring_attn_step_jobs")
 

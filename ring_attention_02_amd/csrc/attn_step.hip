@@ -70,8 +70,20 @@ struct QJob {
   int32_t accumulate, n_seg;
   KvSeg seg[kMaxSegs];
 };
+// Byte ranges the launch forwards around the ring while it computes, in
+// 16-byte units; fwd_end holds inclusive prefix sums (entries past n_fwd
+// repeat the total) and each workgroup moves fwd_per_wg consecutive units.
+constexpr int kMaxFwd = 4;
+struct FwdCopy {
+  u32x4* dst;
+  const u32x4* src;
+};
 struct JobArgs {
   QJob job[kMaxJobs];
+  FwdCopy fwd[kMaxFwd];
+  int64_t fwd_end[kMaxFwd];
+  int64_t fwd_per_wg;
+  int32_t n_fwd;
   int64_t sq;
   int32_t n_jobs, hq, hkv, group;
   int32_t n_qtiles, total_wgs;
@@ -137,6 +149,66 @@ __device__ __forceinline__ int vswz(int c, int r) {
   else return c ^ (4 * ((r >> 1) & 1));                // rows of 128 bytes
 }
 
+// This workgroup's slice of the forwarded ranges: 16-byte units
+// [wg * fwd_per_wg, ...) of their concatenation.  The first round (four units
+// per thread) is split in two so its loads can be issued before the
+// prologue's K/V loads and its stores after them; any further rounds run
+// range by range.  Lanes past the end load an in-bounds unit and store
+// nothing, so the loads need no branches.
+template <int NT>
+struct FwdSlice {
+  u32x4 x[4];
+  u32x4* d[4];
+
+  __device__ __forceinline__ void load_first(const JobArgs& a, int wg, int tid) {
+    const int64_t u0 = static_cast<int64_t>(wg) * a.fwd_per_wg;
+    const int64_t u1 = min(u0 + a.fwd_per_wg, a.fwd_end[kMaxFwd - 1]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t u = u0 + r * NT + tid;
+      const bool valid = u < u1;
+      const int64_t uc = valid ? u : u1 - 1;   // u1 >= 1: every launch forwards >= 1 unit
+      const u32x4* src = a.fwd[0].src;
+      u32x4* dst = a.fwd[0].dst;
+      int64_t start = 0;
+#pragma unroll
+      for (int i = 1; i < kMaxFwd; ++i) {
+        const bool later = uc >= a.fwd_end[i - 1];
+        src = later ? a.fwd[i].src : src;
+        dst = later ? a.fwd[i].dst : dst;
+        start = later ? a.fwd_end[i - 1] : start;
+      }
+      x[r] = src[uc - start];
+      d[r] = valid ? dst + (uc - start) : nullptr;
+    }
+  }
+
+  __device__ __forceinline__ void store_first_and_rest(const JobArgs& a, int wg, int tid) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (d[r] != nullptr) *d[r] = x[r];
+    const int64_t u0 = static_cast<int64_t>(wg) * a.fwd_per_wg + 4 * NT;
+    const int64_t u1 = min(static_cast<int64_t>(wg) * a.fwd_per_wg + a.fwd_per_wg, a.fwd_end[kMaxFwd - 1]);
+    if (u0 >= u1) return;
+#pragma unroll
+    for (int f = 0; f < kMaxFwd; ++f) {
+      const int64_t start = f == 0 ? 0 : a.fwd_end[f - 1];
+      const int64_t lo = max(u0, start) - start, hi = min(u1, a.fwd_end[f]) - start;
+      if (lo >= hi) continue;
+      const u32x4* __restrict__ src = a.fwd[f].src;
+      u32x4* __restrict__ dst = a.fwd[f].dst;
+      for (int64_t base = lo + tid; base < hi + tid; base += 4 * NT) {
+        u32x4 y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = src[min(base + r * NT, hi - 1)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (base + r * NT < hi) dst[base + r * NT] = y[r];
+      }
+    }
+  }
+};
+
 // SPLIT = 2 doubles the waves of a workgroup: waves 4-7 sweep the odd key
 // tiles of the same 128 query rows while waves 0-3 sweep the even ones, and
 // the two softmax states are merged through LDS at the end.  This keeps two
@@ -157,6 +229,10 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   const int half = SPLIT == 1 ? 0 : wave_all >> 2;  // which alternate key tiles it sweeps
   uint16_t* const Kh = Ks + half * 2 * C::KTILE;
   uint16_t* const Vh = Vs + half * 2 * C::VTILE;
+  // Loads of this workgroup's first slice of the forwarded block go out first.
+  FwdSlice<kThreads * SPLIT> fwd;
+  if (a.n_fwd > 0) fwd.load_first(a, blockIdx.x, tid);
+
   const int col = lane & 31;  // query row within the wave (B / C column)
   const int hh = lane >> 5;   // which half of each contraction slice this lane holds
   const int g = lane >> 4;    // 16-lane group (transposed V reads)
@@ -433,17 +509,21 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
     }
   };
 
+  // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight
+  if (my_n > 0) dma_k(tile(0), 0);
+  if (my_n > 1) dma_k(tile(1), 1);
+  if (my_n > 0) dma_v(tile(0), 0);
+  // Stores of this workgroup's slice of the forwarded block (its loads were
+  // issued first); they drain under the prologue's wait.
+  if (a.n_fwd > 0) fwd.store_first_and_rest(a, blockIdx.x, tid);
+
   if (n_iter > 0) {
     f32x16 s_cur[2], s_nxt[2];
     bf16x8 pb[4];
     // Iteration j: [scores of tile j+1 on MFMA + softmax of tile j] then
     // [P_j V_j].  (Running the two key-split halves in opposite phase orders
     // was measured slower on gfx950 than this lock-step order.)
-    // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight;
-    // scores of tile 0
-    if (my_n > 0) dma_k(tile(0), 0);
-    if (my_n > 1) dma_k(tile(1), 1);
-    if (my_n > 0) dma_v(tile(0), 0);
+    // scores of tile 0 once the prologue's loads have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (my_n > 0) qk(0, s_cur);
@@ -685,6 +765,7 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
            "ring_attn_step: %lld workgroups exceed the grid limit", static_cast<long long>(total));
   args.n_qtiles = static_cast<int32_t>(n_qtiles);
   args.total_wgs = static_cast<int32_t>(total);
+  if (args.n_fwd > 0) args.fwd_per_wg = (args.fwd_end[kMaxFwd - 1] + total - 1) / total;
   const dim3 grid(static_cast<unsigned>(total));
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
@@ -711,6 +792,12 @@ bool head_dims_ok(int32_t d_qk, int32_t d_v) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Do the byte ranges [x, x + nx) and [y, y + ny) share a byte?
+inline bool overlaps(const void* x, int64_t nx, const void* y, int64_t ny) {
+  if (x == nullptr || y == nullptr || nx <= 0 || ny <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
+  return a0 < b0 + static_cast<uintptr_t>(ny) && b0 < a0 + static_cast<uintptr_t>(nx);
+}
 
 }  // namespace
 }  // namespace ringattn
@@ -790,7 +877,8 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
   return ok();
 }
 
-extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs, int32_t dtype,
+extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs,
+                                       const cp_copy_t* forward, int32_t n_forward, int32_t dtype,
                                        int32_t batch, int64_t sq, int32_t hq, int32_t hkv,
                                        int32_t d_qk, int32_t d_v, int32_t mask, float scale,
                                        void* stream) {
@@ -825,16 +913,54 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
                "ring_attn_step_jobs: job %d segment %d needs 16-byte aligned k/v", j, sg);
     }
     // concurrent jobs must not write the same output rows
-    for (int i = 0; i < j; ++i) {
-      const auto overlap = [](const void* x, const void* y, int64_t n) {
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
-        return a0 < b0 + n && b0 < a0 + n;
-      };
-      RA_CHECK(!overlap(jobs[i].o, jb.o, o_bytes) && !overlap(jobs[i].lse, jb.lse, lse_bytes),
+    for (int i = 0; i < j; ++i)
+      RA_CHECK(!overlaps(jobs[i].o, o_bytes, jb.o, o_bytes) &&
+                   !overlaps(jobs[i].lse, lse_bytes, jb.lse, lse_bytes),
                CP_EINVAL, "ring_attn_step_jobs: jobs %d and %d write overlapping outputs", i, j);
+  }
+  // Forwarded ranges: aligned, and every destination disjoint from all else
+  // the launch reads or writes.
+  RA_CHECK(n_forward >= 0 && n_forward <= kMaxFwd && (n_forward == 0 || forward != nullptr),
+           CP_EINVAL, "ring_attn_step_jobs: n_forward=%d outside [0, %d]", n_forward, kMaxFwd);
+  for (int f = 0; f < n_forward; ++f) {
+    const cp_copy_t& c = forward[f];
+    RA_CHECK(c.bytes >= 0 && c.bytes % 16 == 0, CP_EINVAL,
+             "ring_attn_step_jobs: forward %d has %lld bytes (a non-negative multiple of 16)", f,
+             static_cast<long long>(c.bytes));
+    if (c.bytes == 0) continue;
+    RA_CHECK(c.dst && c.src && aligned16(c.dst) && aligned16(c.src), CP_EINVAL,
+             "ring_attn_step_jobs: forward %d needs 16-byte aligned device pointers", f);
+    for (int g = 0; g < n_forward; ++g) {
+      RA_CHECK(!overlaps(c.dst, c.bytes, forward[g].src, forward[g].bytes) &&
+                   (g == f || !overlaps(c.dst, c.bytes, forward[g].dst, forward[g].bytes)),
+               CP_EINVAL, "ring_attn_step_jobs: forward %d overlaps forward %d", f, g);
+    }
+    if (rows == 0) continue;
+    for (int j = 0; j < n_jobs; ++j) {
+      const cp_attn_job_t& jb = jobs[j];
+      bool hit = overlaps(c.dst, c.bytes, jb.q, rows * d_qk * 2) ||
+                 overlaps(c.dst, c.bytes, jb.o, o_bytes) || overlaps(c.dst, c.bytes, jb.lse, lse_bytes);
+      for (int sg = 0; sg < jb.n_segments; ++sg) {
+        const cp_kv_segment_t& sgm = jb.segments[sg];
+        const int64_t kv_rows = static_cast<int64_t>(batch) * sgm.sk * hkv;
+        hit = hit || overlaps(c.dst, c.bytes, sgm.k, kv_rows * d_qk * 2) ||
+              overlaps(c.dst, c.bytes, sgm.v, kv_rows * d_v * 2);
+      }
+      RA_CHECK(!hit, CP_EINVAL, "ring_attn_step_jobs: forward %d overlaps a buffer of job %d", f, j);
     }
   }
-  if (rows == 0) return ok();
+  // Without attention work the forwarded ranges still move, as a plain copy.
+  const auto forward_alone = [&]() -> int32_t {
+    if (n_forward == 0) return ok();
+    void* dsts[kMaxFwd];
+    const void* srcs[kMaxFwd];
+    int64_t bytes[kMaxFwd];
+    for (int f = 0; f < n_forward; ++f) {
+      dsts[f] = forward[f].dst; srcs[f] = forward[f].src; bytes[f] = forward[f].bytes;
+    }
+    return ring_stage_copy(dsts, srcs, bytes, n_forward, stream);
+  };
+  if (rows == 0) return forward_alone();
 
   JobArgs ja{};
   bool any_diag = false, any_work = false;
@@ -854,7 +980,16 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
     qj.n_seg = n;
     any_work |= n > 0 || !jb.accumulate;   // a job without keys still writes its empty partial
   }
-  if (!any_work) return ok();
+  if (!any_work) return forward_alone();
+  int64_t units = 0;
+  for (int f = 0; f < kMaxFwd; ++f) {
+    if (f < n_forward) {
+      ja.fwd[f] = FwdCopy{static_cast<u32x4*>(forward[f].dst), static_cast<const u32x4*>(forward[f].src)};
+      units += forward[f].bytes / 16;
+    }
+    ja.fwd_end[f] = units;
+  }
+  ja.n_fwd = units > 0 ? n_forward : 0;
   ja.sq = sq; ja.n_jobs = n_jobs; ja.hq = hq; ja.hkv = hkv; ja.group = hq / hkv;
   ja.causal = mask == CP_MASK_CAUSAL;
   ja.reverse_q = any_diag;   // heaviest query tiles first

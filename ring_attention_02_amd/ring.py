@@ -9,13 +9,14 @@ final result.  With the head-tail partition (vLLM-Ascend "Context Parallel
 sequence parts s and 2N-1-s.
 
 On one GPU the other ranks' K/V live in one full-sequence buffer.  Receiving
-a block is a device-to-device copy on a side stream into one of two staging
-slots, issued one step ahead, so the copy of block t+1 overlaps the
-attention of block t: the double buffering of the video "How Context
-Parallelism Splits Long Sequences Across GPUs" (chapter on the wire budget)
-and of the Excalidraw "Context Parallel (CP) / Ring Attention" diagram
-(rotation overlapped with local attention).  Step 0 uses the rank's own
-block in place.
+a block is a copy into one of two staging slots, made one step ahead so it
+overlaps the attention of the current block: the double buffering of the
+video "How Context Parallelism Splits Long Sequences Across GPUs" (chapter
+on the wire budget) and of the Excalidraw "Context Parallel (CP) / Ring
+Attention" diagram (rotation overlapped with local attention).  The copy
+rides in the ring step's own launch (its forwarded ranges), so a sweep is
+one stream of one launch per step.  Step 0 uses the rank's own block in
+place.
 """
 
 import math
@@ -52,25 +53,17 @@ class ZigzagRing:
                      for _ in range(2)]
         self.vbuf = [torch.empty((2, 1, c, *v_full.shape[2:]), dtype=v_full.dtype, device=dev)
                      for _ in range(2)]
-        self.side = torch.cuda.Stream(device=dev)          # default priority
-        self.ready = [torch.cuda.Event() for _ in range(2)]
-        self.free = [torch.cuda.Event() for _ in range(2)]
-        self.pending_free = [False, False]
 
     def local_slices(self, t):
         return [self.k_full[:, p * self.chunk:(p + 1) * self.chunk] for p in self.steps[t]], \
                [self.v_full[:, p * self.chunk:(p + 1) * self.chunk] for p in self.steps[t]]
 
-    def _stage(self, t):
-        """Side stream: 'receive' the block of step t into slot t % 2."""
-        torch = _torch()
+    def forward_pairs(self, t):
+        """(dst, src) pieces that 'receive' the block of step t into slot t % 2."""
         slot = t % 2
-        if self.pending_free[slot]:
-            self.side.wait_event(self.free[slot])
         ks, vs = self.local_slices(t)
-        stage_copy([(self.kbuf[slot][0], ks[0]), (self.kbuf[slot][1], ks[1]),
-                    (self.vbuf[slot][0], vs[0]), (self.vbuf[slot][1], vs[1])], stream=self.side)
-        self.ready[slot].record(self.side)
+        return [(self.kbuf[slot][0], ks[0]), (self.kbuf[slot][1], ks[1]),
+                (self.vbuf[slot][0], vs[0]), (self.vbuf[slot][1], vs[1])]
 
     def pairs(self):
         """(step, q part index, kv part index, class) for every pair of the sweep."""
@@ -85,24 +78,19 @@ class ZigzagRing:
     def run(self, q_local, o, lse, scale=None, on_launch=None):
         """Sweep every ring step; o [1, 2c, hq, dv] / lse [1, 2c, hq] end final.
 
+        Step t's launch computes with the block of step t and carries the
+        copy of the block of step t + 1 into the other slot.
         on_launch(step, q_index, kv_index, cls, fn) may wrap each launch (the
         bench uses it to time launches); fn() performs the launch.
         """
-        torch = _torch()
-        main = torch.cuda.current_stream()
-        self.side.wait_stream(main)      # inputs written on the main stream are visible
         c = self.chunk
         first = [True, True]
-        if self.cp > 1:
-            self._stage(1)
         for t, kv_parts in enumerate(self.steps):
             if t == 0:
                 ks, vs = self.local_slices(0)
             else:
-                main.wait_event(self.ready[t % 2])
                 ks, vs = self.kbuf[t % 2], self.vbuf[t % 2]
-            if 1 <= t and t + 1 < self.cp:
-                self._stage(t + 1)
+            fwd = self.forward_pairs(t + 1) if t + 1 < self.cp else []
             # One launch per ring step: each local Q part is a job over the
             # block's parts it can see (SKIP parts are left out).
             jobs, step_cls = [], FULL
@@ -120,20 +108,18 @@ class ZigzagRing:
                     jobs.append(dict(q=q_local[:, qs], o=o[:, qs], lse=lse[:, qs],
                                      q_pos0=qp * c, accumulate=acc, segments=segs))
             if jobs:
+                def fn(j=jobs, f=fwd):
+                    ring_attn_step_jobs(j, causal=True, scale=scale, forward=f)
                 if on_launch is None:
-                    ring_attn_step_jobs(jobs, causal=True, scale=scale)
+                    fn()
                 else:
-                    on_launch(t, 0, 0, step_cls,
-                              lambda j=jobs: ring_attn_step_jobs(j, causal=True, scale=scale))
-            if t >= 1:
-                self.free[t % 2].record(main)
-                self.pending_free[t % 2] = True
-        # the staging buffers are reused by the next sweep only after this one
-        main.wait_stream(self.side)
+                    on_launch(t, 0, 0, step_cls, fn)
+            elif fwd:
+                stage_copy(fwd)
         return o, lse
 
     def capture(self, q_local, o, lse, scale=None):
-        """Record one whole sweep (copies, events and kernels) as a HIP graph.
+        """Record one whole sweep as a HIP graph.
 
         Replaying the graph runs the same launches as run() without the
         host-side cost of issuing them one by one; the buffers passed here
@@ -144,13 +130,10 @@ class ZigzagRing:
         graph = torch.cuda.CUDAGraph()
         stream = torch.cuda.Stream()                      # default priority
         stream.wait_stream(torch.cuda.current_stream())
-        saved = list(self.pending_free)
-        self.pending_free = [False, False]               # no cross-replay waits inside the graph
         with torch.cuda.stream(stream):
             with torch.cuda.graph(graph, stream=stream):
                 self.run(q_local, o, lse, scale=scale)
         torch.cuda.current_stream().wait_stream(stream)
-        self.pending_free = saved
         torch.cuda.synchronize()
         return graph
 

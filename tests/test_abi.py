@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(ra):
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
-    assert ra.lib().cp_abi_version() == 1
+    assert ra.lib().cp_abi_version() == 2
     assert ra.lib().cp_status_string(1).decode().startswith("CP_EINVAL")
 
 
@@ -188,9 +188,11 @@ def test_jobs_validate_before_launch(ra):
             j.segments[s] = m._KvSegment(4096, 8192, 16, 0)
         return j
 
-    def call(jobs, dtype=0, dqk=128, dv=128):
+    def call(jobs, dtype=0, dqk=128, dv=128, fwd=()):
         arr = (m._AttnJob * len(jobs))(*jobs)
-        return lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs), dtype, 1, 16,
+        f = (m._Copy * max(1, len(fwd)))(*fwd)
+        return lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), len(jobs),
+                                       ctypes.cast(f, ctypes.c_void_p), len(fwd), dtype, 1, 16,
                                        4, 4, dqk, dv, 1, 0.1, None)
 
     o_bytes = 16 * 4 * 128 * 4
@@ -203,5 +205,16 @@ def test_jobs_validate_before_launch(ra):
     assert call([a], dqk=96, dv=96) == ra.CP_EUNSUPPORTED
     assert call([job(1 << 20 | 8, 2 << 20, 3 << 20)]) == ra.CP_EINVAL      # misaligned q
     arr = (m._AttnJob * 5)(*([a] * 5))
-    assert lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), 5, 0, 1, 16, 4, 4, 128, 128,
-                                   1, 0.1, None) == ra.CP_EINVAL
+    assert lib.ring_attn_step_jobs(ctypes.cast(arr, ctypes.c_void_p), 5, None, 0, 0, 1, 16, 4, 4,
+                                   128, 128, 1, 0.1, None) == ra.CP_EINVAL
+    # forwarded ranges: count, size, alignment and overlap with the jobs' buffers
+    cp = m._Copy
+    free = 64 << 20
+    assert call([a], fwd=[cp(free, 32 << 20, 4096)] * 5) == ra.CP_EINVAL
+    assert call([a], fwd=[cp(free, 32 << 20, 100)]) == ra.CP_EINVAL and "multiple of 16" in ra.last_error()
+    assert call([a], fwd=[cp(free + 8, 32 << 20, 4096)]) == ra.CP_EINVAL
+    assert call([a], fwd=[cp(2 << 20, 32 << 20, 4096)]) == ra.CP_EINVAL       # onto job 0's o
+    assert "job 0" in ra.last_error()
+    assert call([a], fwd=[cp(4096, 32 << 20, 64)]) == ra.CP_EINVAL            # onto segment k
+    assert call([a], fwd=[cp(free, 32 << 20, 4096), cp(free + 2048, 48 << 20, 4096)]) == ra.CP_EINVAL
+    assert call([a], fwd=[cp(free, free + 1024, 4096)]) == ra.CP_EINVAL       # dst overlaps own src

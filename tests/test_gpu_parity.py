@@ -328,7 +328,30 @@ def test_jobs_union_of_segments(ra, dqk, dv, hq, hkv):
         else:
             ro, rl = np.zeros((1, sq, hq, dv)), np.full((1, sq, hq), -np.inf)
         refs.append((o, lse, ro, rl))
-    ra.ring_attn_step_jobs(jobs, causal=True)
+    # the same launch forwards four ranges of odd sizes (copied bit for bit)
+    src = [torch.randn(n, device="cuda") for n in (4096, 4, 100004, 12)]
+    dst = [torch.full_like(x, -1.0) for x in src]
+    ra.ring_attn_step_jobs(jobs, causal=True, forward=list(zip(dst, src)))
     torch.cuda.synchronize()
     for i, (o, lse, ro, rl) in enumerate(refs):
         compare(host64(o), host64(lse), ro, rl, BF16_O, BF16_LSE, f"job {i}")
+    for d, s_ in zip(dst, src):
+        assert torch.equal(d, s_)
+
+
+def test_jobs_forward_without_attention_work(ra):
+    """A launch whose only job has no visible key and accumulates still moves
+    its forwarded ranges (and leaves o / lse as they were)."""
+    q = torch.randn((1, 64, 2, 128), device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, 64, 2, 128), device="cuda").to(torch.bfloat16)
+    o = torch.full((1, 64, 2, 128), 5.0, device="cuda")
+    lse = torch.full((1, 64, 2), 2.0, device="cuda")
+    src = torch.randn((3, 1000, 8), device="cuda")
+    dst = torch.zeros_like(src)
+    ra.ring_attn_step_jobs([dict(q=q, o=o, lse=lse, q_pos0=0, accumulate=True,
+                                 segments=[(k, k, 1000)])],
+                           causal=True, forward=[(dst[0], src[2]), (dst[2], src[0])])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[0], src[2]) and torch.equal(dst[2], src[0])
+    assert bool((dst[1] == 0).all())
+    assert bool((o == 5.0).all()) and bool((lse == 2.0).all())
