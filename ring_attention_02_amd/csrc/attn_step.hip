@@ -262,51 +262,29 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
 
   // The job's segments, each with the number of its tiles that some row of
   // this workgroup can see; the sweep walks them segment after segment
-  // ("virtual" tile numbers).  Everything here is uniform over the workgroup
-  // and kept in named scalars: a per-lane array would be indexed per lane.
-  struct Seg {
-    const uint16_t* k;
-    const uint16_t* v;
-    int64_t sk, k_pos0;
-    int tiles;
-  };
-  auto load_seg = [&](int sg) -> Seg {
-    Seg r{nullptr, nullptr, 0, 0, 0};
-    if (sg < job.n_seg) {
-      const KvSeg& x = job.seg[sg];
-      r.k = static_cast<const uint16_t*>(x.k);
-      r.v = static_cast<const uint16_t*>(x.v);
-      r.sk = x.sk;
-      r.k_pos0 = x.k_pos0;
-      int64_t nkeys = x.sk;
-      if (a.causal) {
-        const int64_t lim = job.q_pos0 + q_last - x.k_pos0 + 1;
-        nkeys = lim < 0 ? 0 : (lim < nkeys ? lim : nkeys);
-      }
-      r.tiles = static_cast<int>((nkeys + kBN - 1) / kBN);
+  // ("virtual" tile numbers).  The cursors below read a segment's fields
+  // from the argument block (uniform scalar loads) only when the sweep
+  // enters it, so no segment state occupies registers in between.
+  auto seg_tiles = [&](int sg) -> int {
+    if (sg >= job.n_seg) return 0;
+    const KvSeg& x = job.seg[sg];
+    int64_t nkeys = x.sk;
+    if (a.causal) {
+      const int64_t lim = job.q_pos0 + q_last - x.k_pos0 + 1;
+      nkeys = lim < 0 ? 0 : (lim < nkeys ? lim : nkeys);
     }
-    return r;
+    return static_cast<int>((nkeys + kBN - 1) / kBN);
   };
-  static_assert(kMaxSegs == 4, "segment selection below is written for four segments");
-  const Seg seg0 = load_seg(0), seg1 = load_seg(1), seg2 = load_seg(2), seg3 = load_seg(3);
-  const int ntiles = seg0.tiles + seg1.tiles + seg2.tiles + seg3.tiles;
-  // virtual tile vt -> its segment, and the tile within it in *t
-  auto locate = [&](int vt, int* t) -> Seg {
-    Seg r = seg0;
-    if (vt >= seg0.tiles) {
-      vt -= seg0.tiles;
-      r = seg1;
-      if (vt >= seg1.tiles) {
-        vt -= seg1.tiles;
-        r = seg2;
-        if (vt >= seg2.tiles) {
-          vt -= seg2.tiles;
-          r = seg3;
-        }
-      }
+  static_assert(kMaxSegs == 4, "four segment slots per job");
+  const int ntiles = seg_tiles(0) + seg_tiles(1) + seg_tiles(2) + seg_tiles(3);
+  // Moves a cursor (segment sg covering virtual tiles [start, end)) forward
+  // to the segment that holds virtual tile vt < ntiles.
+  auto advance = [&](int& sg, int& start, int& end, int vt) {
+    while (vt >= end && sg < kMaxSegs - 1) {
+      ++sg;
+      start = end;
+      end = start + seg_tiles(sg);
     }
-    *t = vt;
-    return r;
   };
 
   // Q^T fragment (B operand): for step c the lane holds Q[row][16c + 8hh .. +7].
@@ -329,12 +307,15 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   float m_run = kNegInf;  // running max of raw scores of this lane's row (possibly stale by < tau)
   float l_run = 0.f;      // running sum over this lane's half of the keys
 
-  // Direct buffer->LDS loads.  Per tile one buffer descriptor covers the
-  // tile's rows of this (batch, kv head); rows past the end of the segment lie
-  // beyond its record count and read as zeros (their scores are masked), so
-  // no tile needs a separate tail path.  Wave-instruction i fills 64
-  // consecutive 16-byte LDS slots; each lane fetches the logical chunk the
-  // swizzle maps to its slot.  Byte offsets inside a tile are loop-invariant.
+  // Direct buffer->LDS loads.  Each of K and V has a cursor: a buffer
+  // descriptor based at some tile of the current segment, whose record count
+  // ends at the segment's last key of this (batch, kv head), and the tile
+  // offset goes in the uniform soffset.  Rows past the end of the segment
+  // read as zeros (their scores are masked), so no tile needs a tail path.
+  // The descriptor is rebuilt only when the sweep enters a segment or has
+  // moved 2^30 bytes past its base.  Wave-instruction i fills 64 consecutive
+  // 16-byte LDS slots; each lane fetches the logical chunk the swizzle maps
+  // to its slot, at a loop-invariant byte offset inside the tile.
   const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
   const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
   uint32_t koffb[C::KDMA], voffb[C::VDMA];
@@ -350,39 +331,49 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
     const int row = p / C::VCPR;
     voffb[i] = static_cast<uint32_t>((row * row_elems_v + vswz<C::VCPR>(p % C::VCPR, row) * 8) * 2);
   }
-  // Descriptor of tile t of segment sgm for K (is_k) or V.
-  auto tile_rsrc = [&](const Seg& sgm, int t, bool is_k) {
+  const int tile_bytes_k = static_cast<int>(kBN * row_elems_k * 2);
+  const int tile_bytes_v = static_cast<int>(kBN * row_elems_v * 2);
+  const int rebase_k = (1 << 30) / tile_bytes_k, rebase_v = (1 << 30) / tile_bytes_v;
+  struct DmaCursor {
+    int sg, start, end, base_vt;
+    __amdgpu_buffer_rsrc_t rsrc;
+  };
+  auto seek = [&](DmaCursor& c, int vt, bool is_k) {
+    advance(c.sg, c.start, c.end, vt);
+    const KvSeg& x = job.seg[c.sg];
     const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
     const int width = is_k ? DQK : DV;
-    const uint16_t* base = (is_k ? sgm.k : sgm.v) + (static_cast<int64_t>(b) * sgm.sk * a.hkv + kvh) * width;
-    const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    // bytes from the tile start to the end of key sk-1's row of this head
-    const int64_t valid = ((sgm.sk - 1 - key0) * row_elems + width) * 2;
+    const uint16_t* base = static_cast<const uint16_t*>(is_k ? x.k : x.v) +
+                           (static_cast<int64_t>(b) * x.sk * a.hkv + kvh) * width;
+    const int64_t key0 = static_cast<int64_t>(vt - c.start) * kBN;
+    // bytes from the base tile to the end of key sk-1's row of this head
+    const int64_t valid = ((x.sk - 1 - key0) * row_elems + width) * 2;
     const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
-                                             static_cast<short>(0), nrec, 0x00020000);
+    c.base_vt = vt;
+    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
+                                               static_cast<short>(0), nrec, 0x00020000);
   };
+  const auto no_rsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(nullptr), static_cast<short>(0), 0, 0);
+  DmaCursor kcur{-1, 0, 0, 0, no_rsrc}, vcur{-1, 0, 0, 0, no_rsrc};
   auto dma_k = [&](int vt, int stage) {
-    int t;
-    const Seg sgm = locate(vt, &t);
-    const auto rsrc = tile_rsrc(sgm, t, true);
+    if (vt >= kcur.end || vt - kcur.base_vt >= rebase_k) seek(kcur, vt, true);
+    const int soff = (vt - kcur.base_vt) * tile_bytes_k;
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::KDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
-          static_cast<int>(koffb[i]), 0, 0, 0);
+          kcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          static_cast<int>(koffb[i]), soff, 0, 0);
   };
   auto dma_v = [&](int vt, int stage) {
-    int t;
-    const Seg sgm = locate(vt, &t);
-    const auto rsrc = tile_rsrc(sgm, t, false);
+    if (vt >= vcur.end || vt - vcur.base_vt >= rebase_v) seek(vcur, vt, false);
+    const int soff = (vt - vcur.base_vt) * tile_bytes_v;
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
     for (int i = 0; i < C::VDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
-          static_cast<int>(voffb[i]), 0, 0, 0);
+          vcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          static_cast<int>(voffb[i]), soff, 0, 0);
   };
 
   // One K fragment (A operand of S^T = K Q^T): key 32kb + col, d chunk 2c + hh.
@@ -430,15 +421,32 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
       if (i + 2 < 4 * C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
+  // Masking cursor of this wave: the segment of the tile being softmaxed and
+  // the first of its tiles in which some key is past the segment end or, for
+  // a causal mask, later than this wave's first query.
+  struct MaskCursor {
+    int sg, start, end, mask_from;
+    int64_t sk, k_pos0;
+  };
+  MaskCursor mcur{-1, 0, 0, 0, 0, 0};
   auto mask_tile = [&](int vt, f32x16* s) {
-    int t;
-    const Seg sgm = locate(vt, &t);
-    const int64_t sk = sgm.sk, k_pos0 = sgm.k_pos0;
-    const int64_t key0 = static_cast<int64_t>(t) * kBN;
-    const bool need = (key0 + kBN > sk) || (a.causal && k_pos0 + key0 + kBN - 1 > job.q_pos0 + wq0);
-    if (!need) return;
+    if (vt >= mcur.end) {
+      advance(mcur.sg, mcur.start, mcur.end, vt);
+      mcur.sk = job.seg[mcur.sg].sk;
+      mcur.k_pos0 = job.seg[mcur.sg].k_pos0;
+      int64_t from = mcur.sk / kBN;                       // the partial last tile, if any
+      if (a.causal) {
+        // key0 + kBN - 1 > q_pos0 + wq0 - k_pos0  <=>  key0 >= that - kBN + 2
+        const int64_t d = job.q_pos0 + wq0 - mcur.k_pos0 - kBN + 2;
+        const int64_t tc = d <= 0 ? 0 : (d + kBN - 1) / kBN;
+        from = min(from, tc);
+      }
+      mcur.mask_from = mcur.start + static_cast<int>(min(from, static_cast<int64_t>(1) << 30));
+    }
+    if (vt < mcur.mask_from) return;
+    const int64_t key0 = static_cast<int64_t>(vt - mcur.start) * kBN;
     // visible iff local key < min(sk, qpos - k_pos0 + 1)
-    const int64_t lim64 = a.causal ? min(sk, qpos - k_pos0 + 1) : sk;
+    const int64_t lim64 = a.causal ? min(mcur.sk, qpos - mcur.k_pos0 + 1) : mcur.sk;
     const int lim = static_cast<int>(max(min(lim64 - key0, static_cast<int64_t>(kBN)), static_cast<int64_t>(0)));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
