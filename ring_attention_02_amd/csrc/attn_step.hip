@@ -25,6 +25,7 @@
 //  * exp2-domain online softmax; fully visible tiles skip the mask.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "kernels_common.h"
@@ -84,6 +85,7 @@ struct JobArgs {
   int64_t fwd_end[kMaxFwd];
   int64_t fwd_per_wg;
   int32_t n_fwd;
+  int32_t paired;   // two jobs, tile p of job 0 and tile n_qtiles-1-p of job 1 per workgroup
   int64_t sq;
   int32_t n_jobs, hq, hkv, group;
   int32_t n_qtiles, total_wgs;
@@ -213,7 +215,7 @@ struct FwdSlice {
 // tiles of the same 128 query rows while waves 0-3 sweep the even ones, and
 // the two softmax states are merged through LDS at the end.  This keeps two
 // waves per SIMD even when a launch has only one workgroup per CU.
-template <int DQK, int DV, int SPLIT>
+template <int DQK, int DV, int SPLIT, bool PAIRED>
 __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(JobArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   using C = Bf16Cfg<DQK, DV>;
@@ -238,17 +240,34 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   const int g = lane >> 4;    // 16-lane group (transposed V reads)
   const int i16 = lane & 15;
 
-  // Workgroup -> (job, query tile, head, batch), job fastest so every XCD's
-  // contiguous range mixes all jobs and tile weights.
+  // Workgroup -> work items (job, query tile) of one (head, batch).  Plain
+  // launches: one item, job fastest so every XCD's contiguous range mixes
+  // all jobs and tile weights.  Paired launches (two jobs whose tile loads
+  // are complementary, as the two query parts of a head-tail rank at the
+  // diagonal step): item 0 is query tile p of job 0, item 1 is tile
+  // n_qtiles-1-p of job 1, run one after the other.
   const int logical = xcd_contiguous_id(blockIdx.x, a.total_wgs);
-  const int jb = logical % a.n_jobs;
-  int rest = logical / a.n_jobs;
-  int qt = rest % a.n_qtiles;
-  rest /= a.n_qtiles;
+  int jb0, qt0, rest;
+  if constexpr (PAIRED) {
+    jb0 = 0;
+    qt0 = logical % a.n_qtiles;
+    rest = logical / a.n_qtiles;
+  } else {
+    jb0 = logical % a.n_jobs;
+    rest = logical / a.n_jobs;
+    qt0 = rest % a.n_qtiles;
+    rest /= a.n_qtiles;
+    if (a.reverse_q) qt0 = a.n_qtiles - 1 - qt0;
+  }
   const int h = rest % a.hq;
   const int b = rest / a.hq;
-  if (a.reverse_q) qt = a.n_qtiles - 1 - qt;
   const int kvh = h / a.group;
+  if (a.n_fwd > 0) fwd.store_first_and_rest(a, blockIdx.x, tid);
+#pragma unroll 1
+  for (int item = 0; item < (PAIRED ? 2 : 1); ++item) {
+  if (item > 0) __syncthreads();   // the previous item is done with the LDS stages
+  const int jb = item == 0 ? jb0 : 1;
+  const int qt = item == 0 ? qt0 : a.n_qtiles - 1 - qt0;
   const QJob& job = a.job[jb];
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(job.q);
@@ -523,7 +542,6 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   if (my_n > 0) dma_v(tile(0), 0);
   // Stores of this workgroup's slice of the forwarded block (its loads were
   // issued first); they drain under the prologue's wait.
-  if (a.n_fwd > 0) fwd.store_first_and_rest(a, blockIdx.x, tid);
 
   if (n_iter > 0) {
     f32x16 s_cur[2], s_nxt[2];
@@ -568,23 +586,25 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
       mine[(NV - 1) * 64] = l_run;
     }
     __syncthreads();
-    if (half == 1) return;
-    const float m1 = mine[(NV - 2) * 64];
-    const float l1 = mine[(NV - 1) * 64];
-    const float m = fmaxf(m_run, m1);
-    const float m_use = m == kNegInf ? 0.f : m;
-    const float a0 = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 for an empty side
-    const float a1 = fast_exp2((m1 - m_use) * a.scale_log2);
+    if (half == 0) {
+      const float m1 = mine[(NV - 2) * 64];
+      const float l1 = mine[(NV - 1) * 64];
+      const float m = fmaxf(m_run, m1);
+      const float m_use = m == kNegInf ? 0.f : m;
+      const float a0 = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 for an empty side
+      const float a1 = fast_exp2((m1 - m_use) * a.scale_log2);
 #pragma unroll
-    for (int d = 0; d < C::DB; ++d)
+      for (int d = 0; d < C::DB; ++d)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] = oacc[d][i] * a0 + mine[(16 * d + i) * 64] * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_run = m;
+        for (int i = 0; i < 16; ++i) oacc[d][i] = oacc[d][i] * a0 + mine[(16 * d + i) * 64] * a1;
+      l_run = l_run * a0 + l1 * a1;
+      m_run = m;
+    }
   }
 
-  // ---- epilogue: normalise, LSE, optional merge into the running result
-  if (!row_valid) return;
+  // ---- epilogue (the even half): normalise, LSE, optional merge into the
+  // running result
+  if (row_valid && half == 0) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const bool has = m_run != kNegInf && l_tot > 0.f;
   const float inv = has ? 1.f / l_tot : 0.f;
@@ -608,6 +628,8 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
       *reinterpret_cast<f32x4*>(op + dv0) = val;
     }
   if (hh == 0) job.lse[orow] = lse_out;
+  }
+  }   // work items
 #endif
 }
 
@@ -768,7 +790,7 @@ int device_cus() {
 template <int DQK, int DV>
 int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
   const int64_t n_qtiles = (args.sq + kBM - 1) / kBM;
-  const int64_t total = n_qtiles * args.n_jobs * args.hq * batch;
+  const int64_t total = n_qtiles * (args.paired ? 1 : args.n_jobs) * args.hq * batch;
   RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
            "ring_attn_step: %lld workgroups exceed the grid limit", static_cast<long long>(total));
   args.n_qtiles = static_cast<int32_t>(n_qtiles);
@@ -777,13 +799,17 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(total));
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
-      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2>), grid, dim3(2 * kThreads), 0, stream, args);
+      if (args.paired)
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true>), grid, dim3(2 * kThreads), 0, stream, args);
+      else
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false>), grid, dim3(2 * kThreads), 0, stream, args);
       const hipError_t err = hipGetLastError();
       RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
       return CP_OK;
     }
   }
-  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1>), grid, dim3(kThreads), 0, stream, args);
+  RA_CHECK(!args.paired, CP_EUNSUPPORTED, "ring_attn_step: paired launch needs the 8-wave variant");
+  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false>), grid, dim3(kThreads), 0, stream, args);
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
   return CP_OK;
@@ -800,6 +826,44 @@ bool head_dims_ok(int32_t d_qk, int32_t d_v) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Key tiles of one query tile of a job: the tiles of each segment that its
+// last row can see (the kernel's sweep length for that workgroup).
+int job_tiles(const JobArgs& ja, int j, int64_t qt) {
+  const QJob& jb = ja.job[j];
+  const int64_t q_last = std::min(ja.sq, (qt + 1) * kBM) - 1;
+  int tiles = 0;
+  for (int sg = 0; sg < jb.n_seg; ++sg) {
+    int64_t nkeys = jb.seg[sg].sk;
+    if (ja.causal) nkeys = std::max<int64_t>(0, std::min(nkeys, jb.q_pos0 + q_last - jb.seg[sg].k_pos0 + 1));
+    tiles += static_cast<int>((nkeys + kBN - 1) / kBN);
+  }
+  return tiles;
+}
+
+// Should a two-job launch pair query tile p of job 0 with tile n-1-p of job 1
+// in one workgroup?  Only grids of at most one workgroup per CU slot are
+// considered (larger grids balance themselves as workgroups retire), and the
+// paired grid must run as 8-wave workgroups.  Cost model in tiles at a full
+// CU: an 8-wave workgroup (fewer workgroups than two per CU) owns its CU, a
+// 4-wave one shares it with another.
+bool pairing_pays(const JobArgs& ja, int64_t batch, int d_qk) {
+  if (ja.n_jobs != 2) return false;
+  const int64_t n = (ja.sq + kBM - 1) / kBM;
+  const int64_t cus = device_cus();
+  const int64_t plain_wgs = 2 * n * ja.hq * batch, paired_wgs = n * ja.hq * batch;
+  if (plain_wgs > 2 * cus) return false;
+  int max_single = 0, max_pair = 0;
+  for (int64_t p = 0; p < n; ++p) {
+    const int a0 = job_tiles(ja, 0, p), a1 = job_tiles(ja, 1, p), b1 = job_tiles(ja, 1, n - 1 - p);
+    max_single = std::max(max_single, std::max(a0, a1));
+    max_pair = std::max(max_pair, a0 + b1);
+  }
+  // pairing runs in the 8-wave variant only
+  if (d_qk > 128 || paired_wgs >= 2 * cus) return false;
+  const int plain_cost = plain_wgs < 2 * cus ? max_single : 2 * max_single;
+  return 20 * max_pair < 17 * plain_cost;
+}
+
 // Do the byte ranges [x, x + nx) and [y, y + ny) share a byte?
 inline bool overlaps(const void* x, int64_t nx, const void* y, int64_t ny) {
   if (x == nullptr || y == nullptr || nx <= 0 || ny <= 0) return false;
@@ -1001,6 +1065,7 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
   ja.sq = sq; ja.n_jobs = n_jobs; ja.hq = hq; ja.hkv = hkv; ja.group = hq / hkv;
   ja.causal = mask == CP_MASK_CAUSAL;
   ja.reverse_q = any_diag;   // heaviest query tiles first
+  ja.paired = pairing_pays(ja, batch, d_qk) ? 1 : 0;
   ja.scale = scale; ja.scale_log2 = scale * kLog2e;
   const int32_t rc = launch_bf16_any(d_qk, ja, batch, static_cast<hipStream_t>(stream));
   return rc == CP_OK ? ok() : rc;

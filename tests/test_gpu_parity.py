@@ -355,3 +355,32 @@ def test_jobs_forward_without_attention_work(ra):
     assert torch.equal(dst[0], src[2]) and torch.equal(dst[2], src[0])
     assert bool((dst[1] == 0).all())
     assert bool((o == 5.0).all()) and bool((lse == 2.0).all())
+
+
+def test_jobs_paired_diagonal_step(ra):
+    """The head-tail diagonal step in one launch: job 0 = the head part over its
+    own chunk (DIAG), job 1 = the tail part over the head chunk (FULL) and its
+    own chunk (DIAG).  With 64 heads and 4 query tiles the plain grid is 512
+    workgroups, so on a 256-CU device the launch pairs tile p of job 0 with
+    tile 3-p of job 1 in one 8-wave workgroup; results must not change."""
+    c, hq, d = 512, 64, 128
+    q, _ = tensor(91, 1, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    k, _ = tensor(91, 2, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    v, _ = tensor(91, 3, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    o = torch.empty((1, 2 * c, hq, d), device="cuda")
+    lse = torch.empty((1, 2 * c, hq), device="cuda")
+    tail0 = 7 * c        # positions: head part 0..c-1, tail part 7c..8c-1
+    k_head, v_head = k[:, :c].contiguous(), v[:, :c].contiguous()
+    k_tail, v_tail = k[:, c:].contiguous(), v[:, c:].contiguous()
+    jobs = [dict(q=q[:, :c], o=o[:, :c], lse=lse[:, :c], q_pos0=0, accumulate=False,
+                 segments=[(k_head, v_head, 0)]),
+            dict(q=q[:, c:], o=o[:, c:], lse=lse[:, c:], q_pos0=tail0, accumulate=False,
+                 segments=[(k_head, v_head, 0), (k_tail, v_tail, tail0)])]
+    ra.ring_attn_step_jobs(jobs, causal=True)
+    torch.cuda.synchronize()
+    heads = [0, 17, 63]
+    q64 = host64(q)[:, :, heads]
+    k64, v64 = host64(k)[:, :, heads], host64(v)[:, :, heads]
+    pos = np.concatenate([np.arange(c), tail0 + np.arange(c)])
+    ro, rl = oracle.attention_ref(q64, k64, v64, pos, pos, True)
+    compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE, "paired")
