@@ -43,7 +43,23 @@ def parse():
     p.add_argument("--only", default="", help="comma list of secondary workloads to run")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    p.add_argument("--sweep-only", type=int, default=0, metavar="K",
+                   help="only replay the zigzag sweep graph K times (for counter passes)")
     return p.parse_args()
+
+
+def sweep_only(reps):
+    """Replays of the headline sweep alone, so per-dispatch counters average
+    exactly over the sweep's launches (one of each per replay)."""
+    import torch
+    import workloads
+    w = workloads.zigzag_setup(2)
+    graph = w["ring"].capture(w["q_local"], w["o"], w["lse"])
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    print(json.dumps({"sweep_replays": reps, "launches_per_sweep": len(zigzag_launches(w))}),
+          flush=True)
 
 
 def calibrate_copy():
@@ -282,6 +298,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sweep_only:
+        sweep_only(args.sweep_only)
         return
 
     log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
