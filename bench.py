@@ -15,8 +15,8 @@ heads x (2 d_qk + 2 d_v) per sweep / time per sweep.
 
 Also reported in the same line (unless --primary-only): the long zigzag
 prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
-(GB/s against HBM), segmented chunked prefill (MLA shape) and a standalone
-LSE merge, each with the roofline of its dominant kernel, plus the CPU
+(GB/s against HBM), the same decode over paged caches read through block
+tables, segmented chunked prefill (MLA shape) and a standalone LSE merge, each with the roofline of its dominant kernel, plus the CPU
 oracle timed on the host.
 """
 
@@ -193,19 +193,26 @@ def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
                         full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3)
 
 
-def decode_bench(steps, warmup):
+def decode_bench(steps, warmup, paged=False):
     import torch
     import ring_attention_02_amd as ra
     import workloads
-    w = workloads.decode_setup()
+    w = workloads.decode_paged_setup() if paged else workloads.decode_setup()
     o_parts = torch.empty((w["n_shards"], w["B"], w["hq"], w["d"]), device="cuda")
     lse_parts = torch.empty((w["n_shards"], w["B"], w["hq"]), device="cuda")
     o = torch.empty((w["B"], w["hq"], w["d"]), device="cuda")
     lse = torch.empty((w["B"], w["hq"]), device="cuda")
 
+    def decode():
+        if paged:
+            ra.split_kv_decode_paged(w["q"], w["kp"], w["vp"], w["tables"], w["lens"],
+                                     o_parts=o_parts, lse_parts=lse_parts)
+        else:
+            ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
+                               lse_parts=lse_parts)
+
     def step():
-        ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
-                           lse_parts=lse_parts)
+        decode()
         ra.lse_merge(o_parts, lse_parts, o_out=o, lse_out=lse)
 
     sec = time_steps(step, steps, warmup)
@@ -214,8 +221,7 @@ def decode_bench(steps, warmup):
     durs = []
     for _ in range(max(3, min(steps, 10))):
         s.record()
-        ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
-                           lse_parts=lse_parts)
+        decode()
         e.record()
         torch.cuda.synchronize()
         durs.append(s.elapsed_time(e))
@@ -357,6 +363,16 @@ def main():
                 "roofline": roofline_entry("hbm", l3["kernel_gbs"], PEAK_HBM_GBS, "GB/s"),
                 "kernel_ms": round(l3["kernel_ms"], 4)}
             del w3
+            torch.cuda.empty_cache()
+        if not only or "c3p" in only:
+            log("C3 paged: the same decode through per-request block tables")
+            w3p, s3p, l3p = decode_bench(max(3, min(args.steps, 10)), 2, paged=True)
+            sec["decode_gqa_8_shards_paged"] = {
+                "value": round(w3p["bytes"] / s3p / 1e9, 1), "unit": "GB/s",
+                "ms_per_step": round(s3p * 1e3, 4), "bytes_per_step": w3p["bytes"],
+                "roofline": roofline_entry("hbm", l3p["kernel_gbs"], PEAK_HBM_GBS, "GB/s"),
+                "kernel_ms": round(l3p["kernel_ms"], 4)}
+            del w3p
             torch.cuda.empty_cache()
         if not only or "c5" in only:
             log("C5: segmented chunked prefill, MLA shape")

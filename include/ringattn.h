@@ -264,6 +264,35 @@ int32_t split_kv_decode(const void* q, const void* k_shards, const void* v_shard
                         void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * split_kv_decode_paged -- split_kv_decode over a paged KV cache.
+ * [CP] "How it works / Block table": a request's logical KV blocks map to
+ * physical blocks of the device's cache through its block table, and the
+ * slot mapping places every token at block_table[vb] * block_size + offset.
+ * Each shard is one device's cache pool; the decode reads through the table.
+ *
+ *   k_pool, v_pool  [n_shards, num_blocks, block_size, hkv, 128]  bf16, device.
+ *   block_tables    device int32 [n_shards, batch, max_blocks]: physical
+ *                   block of logical block j of (shard, request).  An entry
+ *                   outside [0, num_blocks) is read as an empty block (its
+ *                   tokens take no part), never dereferenced.
+ *   shard_lens      device int64 [n_shards*batch]: local tokens of each
+ *                   (shard, request); token i is row i % block_size of block
+ *                   block_tables[.., i / block_size].  Clipped to
+ *                   [0, max_blocks * block_size].  Required.
+ *   q, o_parts, lse_parts, scale, workspace: as split_kv_decode, with the
+ *   workspace sized by split_kv_decode_workspace(..., t_shard =
+ *   max_blocks * block_size).
+ * block_size must be a positive multiple of 32 (CP_EINVAL).  Same dtype and
+ * head-size support as split_kv_decode.
+ * ---------------------------------------------------------------------- */
+int32_t split_kv_decode_paged(const void* q, const void* k_pool, const void* v_pool, int32_t dtype,
+                              int32_t n_shards, int32_t batch, int32_t num_blocks,
+                              int32_t block_size, const int32_t* block_tables, int32_t max_blocks,
+                              const int64_t* shard_lens, int32_t hq, int32_t hkv, int32_t d_qk,
+                              int32_t d_v, float scale, float* o_parts, float* lse_parts,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * ring_stage_copy -- receive a ring step's K/V block into a staging slot.
  * [RA] ring-topology excerpt (each step a device takes over the K/V block of
  * its predecessor while computing); [VID] chapter on the wire budget and

@@ -27,7 +27,7 @@ ABI_VERSION = 2
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
             "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
-            "ring_attn_step_jobs")
+            "ring_attn_step_jobs", "split_kv_decode_paged")
 
 
 class RingAttnError(RuntimeError):
@@ -65,6 +65,9 @@ _lib.split_kv_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
 _lib.split_kv_decode.restype = _i32
 _lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i32, _i32, _i32,
                                  _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+_lib.split_kv_decode_paged.restype = _i32
+_lib.split_kv_decode_paged.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
+                                       _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 _lib.ring_stage_copy.restype = _i32
 _lib.ring_stage_copy.argtypes = [_vp, _vp, _vp, _i32, _vp]
 
@@ -332,6 +335,46 @@ def split_kv_decode(q, k_shards, v_shards, shard_lens=None, scale=None, o_parts=
     return o_parts, lse_parts
 
 
+def split_kv_decode_paged(q, k_pool, v_pool, block_tables, shard_lens, scale=None, o_parts=None,
+                          lse_parts=None, workspace=None, stream=None):
+    """Per-shard decode partials over paged caches.
+
+    q [B,Hq,D]; k_pool / v_pool [S, num_blocks, block_size, Hkv, D] (one pool
+    per shard); block_tables int32 [S, B, max_blocks] (physical block of each
+    logical block); shard_lens int64 [S, B].  Returns (o_parts [S,B,Hq,Dv],
+    lse_parts [S,B,Hq]).
+    """
+    torch = _torch()
+    B, Hq, Dqk = q.shape
+    S, NB, BS, Hkv, Dk = k_pool.shape
+    Dv = v_pool.shape[4]
+    if Dk != Dqk or tuple(v_pool.shape[:4]) != (S, NB, BS, Hkv):
+        raise ValueError("q / pool shapes do not agree")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 3 or \
+            tuple(block_tables.shape[:2]) != (S, B):
+        raise ValueError("block_tables must be int32 [n_shards, batch, max_blocks]")
+    if shard_lens.dtype != torch.int64 or tuple(shard_lens.shape) != (S, B):
+        raise ValueError("shard_lens must be int64 [n_shards, batch]")
+    MB = block_tables.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if o_parts is None:
+        o_parts = torch.empty((S, B, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((S, B, Hq), dtype=torch.float32, device=q.device)
+    ws_need = split_kv_decode_workspace(S, B, Hq, Hkv, Dv, MB * BS)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    _check(_lib.split_kv_decode_paged(
+        _dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), _dtype_code(q), S, B,
+        NB, BS, _dev_ptr(block_tables, "block_tables"), MB, _dev_ptr(shard_lens, "shard_lens"), Hq, Hkv,
+        Dqk, Dv, float(scale), _dev_ptr(o_parts, "o_parts"), _dev_ptr(lse_parts, "lse_parts"),
+        None if workspace is None else _dev_ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream_handle(stream)), "split_kv_decode_paged")
+    return o_parts, lse_parts
+
+
 def stage_copy(pairs, stream=None):
     """Copy each (dst, src) pair of equally sized contiguous GPU tensors in one launch."""
     n = len(pairs)
@@ -351,6 +394,6 @@ from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E
 
 __all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "ring_attn_step_jobs",
            "lse_merge", "stage_copy",
-           "split_kv_decode", "split_kv_decode_workspace", "ZigzagRing", "segmented_prefill",
+           "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged", "ZigzagRing", "segmented_prefill",
            "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
            "last_error"]

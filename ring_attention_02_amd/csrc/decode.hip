@@ -40,9 +40,11 @@ constexpr int kTargetWgs = 2048;   // enough workgroups to fill 256 CUs several 
 
 struct DecodeArgs {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* k;   // contiguous shards [n_shards, B, t_shard, Hkv, 128], or block pools
+  const uint16_t* v;   // [n_shards, num_blocks, block_size, Hkv, 128] when paged
   const int64_t* shard_lens;
+  const int32_t* block_table;   // paged: [n_shards, B, max_blocks] physical block ids
+  int32_t block_size, max_blocks, num_blocks;
   float* o;    // [rows_out, 128] destination (o_parts, or split-major workspace)
   float* lse;  // [rows_out]
   int64_t t_shard;
@@ -50,6 +52,11 @@ struct DecodeArgs {
   float scale, scale_log2;
 };
 
+// PAGED: token i of (shard, request) lives in block block_table[i / block_size]
+// of the shard's pool, at row i % block_size ([CP] "Block table": the
+// table maps a request's logical blocks to physical blocks).  block_size is a
+// multiple of the 32-key wave tile, so one table entry serves a whole tile.
+template <bool PAGED>
 __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) {
   // Per-wave V tile during the sweep; reused for the cross-wave merge.
   __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kTile * kVPitch];
@@ -93,36 +100,68 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   }
 
   const int64_t row_stride = static_cast<int64_t>(a.hkv) * kD;  // elements between keys
-  const int64_t shard_base =
-      ((static_cast<int64_t>(s) * a.batch + b) * a.t_shard) * row_stride + static_cast<int64_t>(kvh) * kD;
-  const uint16_t* kbase = a.k + shard_base;
-  const uint16_t* vbase = a.v + shard_base;
   uint16_t* vslot = smem + wave * kTile * kVPitch;
+
+  // The wave's 32-key tile of round r: element offset of its first key (from
+  // the K/V base) and how many of its keys exist (0 for a tile past the end
+  // or, paged, in a block whose table entry is outside the pool).
+  struct Tile {
+    int64_t off;
+    int valid;
+  };
+  // Paged: the table entry of a round's tile is fetched one round ahead
+  // with a vector load (it completes in order with the K/V loads issued
+  // after it, so using it never waits on anything the round needs).
+  const int32_t* trow = PAGED ? a.block_table + (static_cast<int64_t>(s) * a.batch + b) * a.max_blocks
+                              : nullptr;
+  const auto trsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(trow), static_cast<short>(0),
+                                                       PAGED ? a.max_blocks * 4 : 0, 0x00020000);
+  auto fetch_entry = [&](int r) -> int32_t {
+    const int64_t t0 = k_begin + static_cast<int64_t>(r) * kRound + wave * kTile;
+    if (!PAGED || t0 >= k_end) return -1;
+    return __builtin_amdgcn_raw_buffer_load_b32(trsrc, static_cast<int>(t0 / a.block_size) * 4, 0, 0);
+  };
+  auto tile_of = [&](int r, int32_t entry) -> Tile {
+    const int64_t t0 = k_begin + static_cast<int64_t>(r) * kRound + wave * kTile;
+    Tile t{0, 0};
+    if (t0 >= k_end) return t;
+    t.valid = static_cast<int>(min(static_cast<int64_t>(kTile), k_end - t0));
+    if constexpr (PAGED) {
+      const int32_t blk = __builtin_amdgcn_readfirstlane(entry);
+      if (blk < 0 || blk >= a.num_blocks) {
+        t.valid = 0;
+        return t;
+      }
+      t.off = ((static_cast<int64_t>(s) * a.num_blocks + blk) * a.block_size + t0 % a.block_size) * row_stride;
+    } else {
+      t.off = ((static_cast<int64_t>(s) * a.batch + b) * a.t_shard + t0) * row_stride;
+    }
+    t.off += static_cast<int64_t>(kvh) * kD;
+    return t;
+  };
 
   // K: lane (key n16 of block kb, g) loads 64 contiguous bytes per block:
   // kreg[kb*4 + c] = K[key][32c + 8g .. +7]  (the A operand of step c).
   // V: lane loads rows 4i + g/... : vreg[i] = V[tile + 4i + lane/16][8*(lane%16) .. +7].
   u32x4 kcur[8], knext[8], vnext[8];
-  auto load_k = [&](int r, u32x4* dst) {
-    const int64_t t0 = k_begin + static_cast<int64_t>(r) * kRound + wave * kTile;
+  auto load_k = [&](const Tile& t, u32x4* dst) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int64_t key = t0 + kb * 16 + n16;
+      const int key = kb * 16 + n16;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (key < k_end) raw = *reinterpret_cast<const u32x4*>(kbase + key * row_stride + 32 * c + 8 * g);
+        if (key < t.valid) raw = *reinterpret_cast<const u32x4*>(a.k + t.off + key * row_stride + 32 * c + 8 * g);
         dst[kb * 4 + c] = raw;
       }
     }
   };
-  auto load_v = [&](int r) {
-    const int64_t t0 = k_begin + static_cast<int64_t>(r) * kRound + wave * kTile;
+  auto load_v = [&](const Tile& t) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t key = t0 + 4 * i + g;
+      const int key = 4 * i + g;
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (key < k_end) raw = *reinterpret_cast<const u32x4*>(vbase + key * row_stride + 8 * n16);
+      if (key < t.valid) raw = *reinterpret_cast<const u32x4*>(a.v + t.off + key * row_stride + 8 * n16);
       vnext[i] = raw;
     }
   };
@@ -132,9 +171,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
+  int32_t entry_cur = fetch_entry(0), entry_next = fetch_entry(1);
+  int32_t entry_now = entry_cur;     // entry of the round being computed
   if (rounds > 0) {
-    load_k(0, kcur);
-    load_v(0);
+    const Tile t = tile_of(0, entry_cur);
+    load_k(t, kcur);
+    load_v(t);
   }
   for (int r = 0; r < rounds; ++r) {
     __syncthreads();
@@ -143,11 +185,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
       *reinterpret_cast<u32x4*>(&vslot[(4 * i + g) * kVPitch + 8 * n16]) = vnext[i];
     __syncthreads();
     if (r + 1 < rounds) {
-      load_k(r + 1, knext);
-      load_v(r + 1);
+      const Tile t = tile_of(r + 1, entry_next);
+      load_k(t, knext);
+      load_v(t);
     }
-    const int64_t t0 = k_begin + static_cast<int64_t>(r) * kRound + wave * kTile;
-    if (t0 < k_end) {
+    const int valid = tile_of(r, entry_now).valid;
+    entry_now = entry_next;
+    if (r + 2 < rounds) entry_next = fetch_entry(r + 2);
+    if (valid > 0) {
       // S^T = K Q^T for two 16-key blocks; acc[kb][j] = score of key
       // t0 + kb*16 + 4g + j for query column n16.
       f32x4 sc[2];
@@ -159,12 +204,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
           sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kcur[kb * 4 + c]),
                                                            qf[c], sc[kb], 0, 0, 0);
       }
-      if (t0 + kTile > k_end) {
+      if (valid < kTile) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (t0 + kb * 16 + 4 * g + j >= k_end) sc[kb][j] = kNegInf;
+            if (kb * 16 + 4 * g + j >= valid) sc[kb][j] = kNegInf;
       }
       float mx = kNegInf;
 #pragma unroll
@@ -275,38 +320,73 @@ extern "C" size_t split_kv_decode_workspace(int32_t n_shards, int32_t batch, int
   return static_cast<size_t>(splits) * rows * (static_cast<size_t>(d_v) + 1) * sizeof(float);
 }
 
+namespace ringattn {
+namespace {
+
+// Checks shared by both decode entry points, then the launch (and the merge
+// of the key splits).  t_shard is the longest local context of a (shard,
+// request): the contiguous shard length, or max_blocks * block_size.
+int32_t run_decode(const char* who, bool paged, DecodeArgs args, int32_t dtype, int32_t d_qk,
+                   int32_t d_v, float* o_parts, float* lse_parts, void* workspace, size_t ws_bytes,
+                   hipStream_t st) {
+  RA_CHECK(dtype == CP_BF16 || dtype == CP_F32, CP_EDTYPE, "%s: dtype=%d", who, dtype);
+  RA_CHECK(dtype == CP_BF16, CP_EUNSUPPORTED, "%s: only bf16 inputs are supported", who);
+  RA_CHECK(args.n_shards > 0 && args.batch >= 0 && args.t_shard >= 0, CP_EINVAL,
+           "%s: bad sizes (n_shards=%d batch=%d tokens=%lld)", who, args.n_shards, args.batch,
+           static_cast<long long>(args.t_shard));
+  RA_CHECK(args.hq > 0 && args.hkv > 0 && args.hq % args.hkv == 0, CP_EINVAL,
+           "%s: hq=%d must be a positive multiple of hkv=%d", who, args.hq, args.hkv);
+  RA_CHECK(d_qk == kD && d_v == kD, CP_EUNSUPPORTED,
+           "%s: only d_qk = d_v = 128 is supported (got %d, %d)", who, d_qk, d_v);
+  RA_CHECK(args.hq / args.hkv <= kMaxGroup, CP_EUNSUPPORTED,
+           "%s: hq/hkv=%d exceeds %d query heads per kv head", who, args.hq / args.hkv, kMaxGroup);
+  RA_CHECK(args.scale > 0.f && args.scale < __builtin_huge_valf(), CP_EINVAL,
+           "%s: scale must be positive and finite", who);
+  if (args.batch == 0) return ok();
+  RA_CHECK(args.q && o_parts && lse_parts && (args.t_shard == 0 || (args.k && args.v)), CP_EINVAL,
+           "%s: NULL pointer", who);
+  RA_CHECK(aligned16(args.q) && aligned16(o_parts) &&
+               (args.t_shard == 0 || (aligned16(args.k) && aligned16(args.v))),
+           CP_EINVAL, "%s: device pointers must be 16-byte aligned", who);
+  const int32_t splits = choose_splits(args.n_shards, args.batch, args.hkv, args.t_shard);
+  const size_t need =
+      split_kv_decode_workspace(args.n_shards, args.batch, args.hq, args.hkv, d_v, args.t_shard);
+  RA_CHECK(ws_bytes >= need && (need == 0 || (workspace && aligned16(workspace))), CP_EINVAL,
+           "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu", who, need, ws_bytes);
+  const int64_t items = static_cast<int64_t>(args.n_shards) * args.batch * args.hkv * splits;
+  RA_CHECK(items < (int64_t{1} << 31), CP_EUNSUPPORTED, "%s: too many work items", who);
+
+  const int64_t rows = static_cast<int64_t>(args.n_shards) * args.batch * args.hq;
+  args.group = args.hq / args.hkv;
+  args.n_splits = splits;
+  args.scale_log2 = args.scale * kLog2e;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o ? ws_o + static_cast<size_t>(splits) * rows * kD : nullptr;
+  args.o = splits > 1 ? ws_o : o_parts;
+  args.lse = splits > 1 ? ws_lse : lse_parts;
+  if (paged)
+    hipLaunchKernelGGL(decode_bf16_kernel<true>, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0,
+                       st, args);
+  else
+    hipLaunchKernelGGL(decode_bf16_kernel<false>, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0,
+                       st, args);
+  hipError_t err = hipGetLastError();
+  RA_CHECK(err == hipSuccess, CP_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
+  if (splits > 1) {
+    const int32_t rc = launch_lse_merge(ws_o, ws_lse, splits, rows, kD, o_parts, CP_F32, lse_parts, st);
+    if (rc != CP_OK) return rc;
+  }
+  return ok();
+}
+
+}  // namespace
+}  // namespace ringattn
+
 extern "C" int32_t split_kv_decode(const void* q, const void* k_shards, const void* v_shards,
                                    int32_t dtype, int32_t n_shards, int32_t batch, int64_t t_shard,
                                    const int64_t* shard_lens, int32_t hq, int32_t hkv, int32_t d_qk,
                                    int32_t d_v, float scale, float* o_parts, float* lse_parts,
                                    void* workspace, size_t ws_bytes, void* stream) {
-  RA_CHECK(dtype == CP_BF16 || dtype == CP_F32, CP_EDTYPE, "split_kv_decode: dtype=%d", dtype);
-  RA_CHECK(dtype == CP_BF16, CP_EUNSUPPORTED, "split_kv_decode: only bf16 inputs are supported");
-  RA_CHECK(n_shards > 0 && batch >= 0 && t_shard >= 0, CP_EINVAL,
-           "split_kv_decode: bad sizes (n_shards=%d batch=%d t_shard=%lld)", n_shards, batch,
-           static_cast<long long>(t_shard));
-  RA_CHECK(hq > 0 && hkv > 0 && hq % hkv == 0, CP_EINVAL,
-           "split_kv_decode: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
-  RA_CHECK(d_qk == kD && d_v == kD, CP_EUNSUPPORTED,
-           "split_kv_decode: only d_qk = d_v = 128 is supported (got %d, %d)", d_qk, d_v);
-  RA_CHECK(hq / hkv <= kMaxGroup, CP_EUNSUPPORTED,
-           "split_kv_decode: hq/hkv=%d exceeds %d query heads per kv head", hq / hkv, kMaxGroup);
-  RA_CHECK(scale > 0.f && scale < __builtin_huge_valf(), CP_EINVAL,
-           "split_kv_decode: scale must be positive and finite");
-  if (batch == 0) return ok();
-  RA_CHECK(q && o_parts && lse_parts && (t_shard == 0 || (k_shards && v_shards)), CP_EINVAL,
-           "split_kv_decode: NULL pointer");
-  RA_CHECK(aligned16(q) && aligned16(o_parts) && (t_shard == 0 || (aligned16(k_shards) && aligned16(v_shards))),
-           CP_EINVAL, "split_kv_decode: device pointers must be 16-byte aligned");
-  const int32_t splits = choose_splits(n_shards, batch, hkv, t_shard);
-  const size_t need = split_kv_decode_workspace(n_shards, batch, hq, hkv, d_v, t_shard);
-  RA_CHECK(ws_bytes >= need && (need == 0 || (workspace && aligned16(workspace))), CP_EINVAL,
-           "split_kv_decode: workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
-           ws_bytes);
-  const int64_t items = static_cast<int64_t>(n_shards) * batch * hkv * splits;
-  RA_CHECK(items < (int64_t{1} << 31), CP_EUNSUPPORTED, "split_kv_decode: too many work items");
-
-  const int64_t rows = static_cast<int64_t>(n_shards) * batch * hq;
   DecodeArgs args{};
   args.q = static_cast<const uint16_t*>(q);
   args.k = static_cast<const uint16_t*>(k_shards);
@@ -314,20 +394,36 @@ extern "C" int32_t split_kv_decode(const void* q, const void* k_shards, const vo
   args.shard_lens = shard_lens;
   args.t_shard = t_shard;
   args.n_shards = n_shards; args.batch = batch; args.hq = hq; args.hkv = hkv;
-  args.group = hq / hkv; args.n_splits = splits;
-  args.scale = scale; args.scale_log2 = scale * kLog2e;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = ws_o ? ws_o + static_cast<size_t>(splits) * rows * kD : nullptr;
-  args.o = splits > 1 ? ws_o : o_parts;
-  args.lse = splits > 1 ? ws_lse : lse_parts;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(decode_bf16_kernel, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0, st,
-                     args);
-  hipError_t err = hipGetLastError();
-  RA_CHECK(err == hipSuccess, CP_EHIP, "split_kv_decode: launch failed: %s", hipGetErrorString(err));
-  if (splits > 1) {
-    const int32_t rc = launch_lse_merge(ws_o, ws_lse, splits, rows, kD, o_parts, CP_F32, lse_parts, st);
-    if (rc != CP_OK) return rc;
-  }
-  return ok();
+  args.scale = scale;
+  return run_decode("split_kv_decode", false, args, dtype, d_qk, d_v, o_parts, lse_parts, workspace,
+                    ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t split_kv_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                                         int32_t dtype, int32_t n_shards, int32_t batch,
+                                         int32_t num_blocks, int32_t block_size,
+                                         const int32_t* block_tables, int32_t max_blocks,
+                                         const int64_t* shard_lens, int32_t hq, int32_t hkv,
+                                         int32_t d_qk, int32_t d_v, float scale, float* o_parts,
+                                         float* lse_parts, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  RA_CHECK(block_size > 0 && block_size % kTile == 0, CP_EINVAL,
+           "split_kv_decode_paged: block_size=%d must be a positive multiple of %d", block_size, kTile);
+  RA_CHECK(num_blocks > 0 && max_blocks >= 0, CP_EINVAL,
+           "split_kv_decode_paged: num_blocks=%d must be positive, max_blocks=%d non-negative",
+           num_blocks, max_blocks);
+  RA_CHECK(batch == 0 || max_blocks == 0 || (block_tables && shard_lens), CP_EINVAL,
+           "split_kv_decode_paged: block_tables and shard_lens are required");
+  DecodeArgs args{};
+  args.q = static_cast<const uint16_t*>(q);
+  args.k = static_cast<const uint16_t*>(k_pool);
+  args.v = static_cast<const uint16_t*>(v_pool);
+  args.shard_lens = shard_lens;
+  args.block_table = block_tables;
+  args.block_size = block_size; args.max_blocks = max_blocks; args.num_blocks = num_blocks;
+  args.t_shard = static_cast<int64_t>(max_blocks) * block_size;
+  args.n_shards = n_shards; args.batch = batch; args.hq = hq; args.hkv = hkv;
+  args.scale = scale;
+  return run_decode("split_kv_decode_paged", true, args, dtype, d_qk, d_v, o_parts, lse_parts,
+                    workspace, ws_bytes, static_cast<hipStream_t>(stream));
 }

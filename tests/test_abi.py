@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 13, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
@@ -218,3 +218,19 @@ def test_jobs_validate_before_launch(ra):
     assert call([a], fwd=[cp(4096, 32 << 20, 64)]) == ra.CP_EINVAL            # onto segment k
     assert call([a], fwd=[cp(free, 32 << 20, 4096), cp(free + 2048, 48 << 20, 4096)]) == ra.CP_EINVAL
     assert call([a], fwd=[cp(free, free + 1024, 4096)]) == ra.CP_EINVAL       # dst overlaps own src
+
+
+def test_decode_paged_validates_before_launch(ra):
+    lib = ra.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    def call(bs=128, nb=16, mb=4, d=128, tables=fake, lens=fake, batch=2):
+        return lib.split_kv_decode_paged(fake, fake, fake, 0, 4, batch, nb, bs, tables, mb, lens,
+                                         8, 1, d, d, 0.1, fake, fake, None, 0, None)
+    assert call(bs=100) == ra.CP_EINVAL and "multiple of 32" in ra.last_error()
+    assert call(bs=0) == ra.CP_EINVAL
+    assert call(nb=0) == ra.CP_EINVAL
+    assert call(mb=-1) == ra.CP_EINVAL
+    assert call(tables=None) == ra.CP_EINVAL
+    assert call(lens=None) == ra.CP_EINVAL
+    assert call(d=64) == ra.CP_EUNSUPPORTED
+    assert call(batch=0) == ra.CP_OK          # nothing to do, nothing launched

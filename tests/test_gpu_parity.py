@@ -384,3 +384,75 @@ def test_jobs_paired_diagonal_step(ra):
     pos = np.concatenate([np.arange(c), tail0 + np.arange(c)])
     ro, rl = oracle.attention_ref(q64, k64, v64, pos, pos, True)
     compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE, "paired")
+
+
+def _decode_paged_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs, il, spare_blocks,
+                       drop=None):
+    """Paged caches: each request has its own block table (a random choice of
+    physical blocks, the same ids in every shard's pool, as the slot mapping
+    places them); tokens go to pool[dev, table[vb] * bs + loc].  drop=(s, b, j)
+    points entry j of (shard s, request b) outside the pool: those tokens
+    must take no part."""
+    d = 128
+    tmax = max(ctx_lens)
+    vbs = bs * n_shards
+    n_vb = [-(-L // vbs) for L in ctx_lens]
+    num_blocks = sum(n_vb) + spare_blocks
+    max_blocks = max(n_vb) + 1
+    rng = np.random.default_rng(cfg)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    q, q64 = tensor(cfg, 1, 0, (B, hq, d), torch.bfloat16)
+    k_ctx, k64 = tensor(cfg, 2, 0, (B, tmax, hkv, d), torch.bfloat16)
+    v_ctx, v64 = tensor(cfg, 3, 0, (B, tmax, hkv, d), torch.bfloat16)
+    kp = torch.zeros((n_shards, num_blocks, bs, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    tables = np.full((n_shards, B, max_blocks), -1, dtype=np.int32)
+    lens = np.zeros((n_shards, B), dtype=np.int64)
+    devs, used = [], 0
+    for b, L in enumerate(ctx_lens):
+        table = perm[used:used + n_vb[b]]
+        used += n_vb[b]
+        dev, slot = ra.slot_mapping(np.arange(L), bs, il, n_shards, 1, block_table=table)
+        devs.append(dev)
+        lens[:, b] = np.bincount(dev, minlength=n_shards)
+        tables[:, b, :n_vb[b]] = table
+        dev_t = torch.from_numpy(dev.astype(np.int64)).cuda()
+        slot_t = torch.from_numpy(slot).cuda()
+        kp.view(n_shards, num_blocks * bs, hkv, d)[dev_t, slot_t] = k_ctx[b, :L]
+        vp.view(n_shards, num_blocks * bs, hkv, d)[dev_t, slot_t] = v_ctx[b, :L]
+    if drop is not None:
+        s, b, j = drop
+        tables[s, b, j] = num_blocks + 5          # outside the pool
+    tables_t = torch.from_numpy(tables).cuda()
+    lens_t = torch.from_numpy(lens).cuda()
+    o_parts, lse_parts = ra.split_kv_decode_paged(q, kp, vp, tables_t, lens_t)
+    o, lse = ra.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    for b, L in enumerate(ctx_lens):
+        dev_ref, slot_ref = oracle.slot_mapping_ref(np.arange(L), bs, il, n_shards, 1)
+        dev_ref = np.asarray(dev_ref).copy()
+        if drop is not None and drop[1] == b:
+            s, _, j = drop
+            # local block j of shard s holds the tokens with local index in [j*bs, (j+1)*bs)
+            dev_ref[(dev_ref == s) & (np.asarray(slot_ref) // bs == j)] = -1
+        po, pl, mo, ml = oracle.decode_shards_ref(q64[b:b + 1], k64[b:b + 1, :L], v64[b:b + 1, :L],
+                                                  dev_ref, n_shards)
+        compare(host64(o_parts[:, b]), host64(lse_parts[:, b]), po[:, 0], pl[:, 0], BF16_O,
+                BF16_LSE, f"paged partials b={b}")
+        compare(host64(o[b]), host64(lse[b]), mo[0], ml[0], BF16_O, BF16_LSE, f"paged b={b}")
+
+
+def test_split_kv_decode_paged(ra):
+    say("paged decode: 8 shards, 3 ragged requests, random block tables, GQA 8")
+    _decode_paged_case(ra, 44, 3, [4096, 1500, 3000], 8, 16, 2, 128, 16, spare_blocks=7)
+
+
+def test_split_kv_decode_paged_splits_and_small_blocks(ra):
+    say("paged decode: 2 shards, blocks of 32, key splits")
+    assert ra.split_kv_decode_workspace(2, 1, 4, 1, 128, 300 * 32) > 0
+    _decode_paged_case(ra, 45, 1, [16384 - 77], 2, 4, 1, 32, 8, spare_blocks=40)
+
+
+def test_split_kv_decode_paged_entry_outside_pool(ra):
+    say("paged decode: one table entry outside the pool is an empty block")
+    _decode_paged_case(ra, 46, 2, [2048, 1000], 4, 8, 1, 64, 16, spare_blocks=3, drop=(1, 0, 2))

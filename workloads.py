@@ -112,6 +112,44 @@ def decode_setup(requests=None):
                 bytes=kv_bytes + q.numel() * 2 + 2 * n_sh * B * hq * (d + 1) * 4 + B * hq * (d + 1) * 4)
 
 
+def decode_paged_setup():
+    """C3 in a paged layout: each shard's cache is a pool of 128-token blocks;
+    request b's virtual blocks take a seeded random choice of physical blocks
+    (the same ids in every shard), and the slot mapping places each token at
+    table[vb] * block_size + loc of its shard's pool."""
+    import ring_attention_02_amd as ra
+    torch = _torch()
+    c = CONFIGS[3]
+    B, hq, hkv, d, ctx = c["batch"], c["hq"], c["hkv"], c["d"], c["ctx"]
+    bs, il, n_sh = c["block_size"], c["interleave"], c["pcp"] * c["dcp"]
+    n_vb = -(-ctx // (bs * n_sh))
+    num_blocks = B * n_vb
+    perm = np.random.default_rng(si.device_seed(3, 9, 0)).permutation(num_blocks).astype(np.int32)
+    kp = torch.empty((n_sh, num_blocks * bs, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    tables = np.empty((n_sh, B, n_vb), dtype=np.int32)
+    lens = np.empty((n_sh, B), dtype=np.int64)
+    for b in range(B):
+        table = perm[b * n_vb:(b + 1) * n_vb]
+        dev, slot = ra.slot_mapping(np.arange(ctx), bs, il, c["pcp"], c["dcp"], block_table=table)
+        tables[:, b] = table
+        lens[:, b] = np.bincount(dev, minlength=n_sh)
+        dev_t = torch.from_numpy(dev.astype(np.int64)).cuda()
+        slot_t = torch.from_numpy(slot).cuda()
+        kc = si.device_normal(3, K_ID, b, (ctx, hkv, d), torch.bfloat16, "cuda")
+        kp[dev_t, slot_t] = kc
+        del kc
+        vc = si.device_normal(3, V_ID, b, (ctx, hkv, d), torch.bfloat16, "cuda")
+        vp[dev_t, slot_t] = vc
+        del vc
+    q = host_tensor(3, Q_ID, 0, (B, hq, d), torch.bfloat16)
+    kv_bytes = 2 * n_sh * B * n_vb * bs * hkv * d * 2
+    return dict(q=q, kp=kp.view(n_sh, num_blocks, bs, hkv, d), vp=vp.view(n_sh, num_blocks, bs, hkv, d),
+                tables=torch.from_numpy(tables).cuda(), lens=torch.from_numpy(lens).cuda(), B=B, hq=hq,
+                hkv=hkv, d=d, ctx=ctx, n_shards=n_sh, kv_bytes=kv_bytes,
+                bytes=kv_bytes + q.numel() * 2 + 2 * n_sh * B * hq * (d + 1) * 4 + B * hq * (d + 1) * 4)
+
+
 def decode_context(b, ctx=None):
     """Token-order K/V context of request b (regenerated from its seed)."""
     torch = _torch()
