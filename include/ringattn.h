@@ -220,6 +220,48 @@ int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs,
                             int32_t d_v, int32_t mask, float scale, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ring_attn_step_varlen -- one ring step for several packed requests.
+ * [CP] PCP head-tail partition paragraph (several requests are split and
+ * laid out one after the other on each device) and chunked-prefill
+ * paragraph; [VID] chapter on kernels and causal masks (per-block masks).
+ *
+ *   q   [total_q, hq, d_qk]  dtype, device (requests packed along tokens).
+ *   k   [total_k, hkv, d_qk], v [total_k, hkv, d_v]  dtype, device.
+ *   o   [total_q, hq, d_v] float32, lse [total_q, hq] float32, device.
+ *   cu_seqlens_q, cu_seqlens_k  HOST int64 [n_req + 1]: request r owns
+ *       query rows [cu_q[r], cu_q[r+1]) and key rows [cu_k[r], cu_k[r+1]);
+ *       total_q = cu_q[n_req], total_k = cu_k[n_req].
+ *   q_pos0, k_pos0  HOST int64 [n_req]: absolute position of each request's
+ *       first query / key.
+ * Every request is an independent ring_attn_step over its own rows: keys of
+ * other requests are never visible; masking, GQA, scale and accumulate are as
+ * for ring_attn_step (a request without visible keys gets O = 0, LSE = -inf,
+ * or is left unchanged when accumulating).  The offsets must start >= 0 and
+ * not decrease, packed lengths stay below 2^31 (CP_EINVAL / CP_EUNSUPPORTED).
+ * bf16 only.  One launch covers up to 64 requests.
+ * ---------------------------------------------------------------------- */
+int32_t ring_attn_step_varlen(const void* q, const void* k, const void* v, int32_t dtype,
+                              int32_t n_req, const int64_t* cu_seqlens_q,
+                              const int64_t* cu_seqlens_k, const int64_t* q_pos0,
+                              const int64_t* k_pos0, int32_t hq, int32_t hkv, int32_t d_qk,
+                              int32_t d_v, int32_t mask, float scale, int32_t accumulate, float* o,
+                              float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * cp_gather_rows -- dst row i = src row idx[i] (device).
+ * [CP] PCP head-tail partition paragraph: after the ranks' outputs are
+ * gathered, the restore index puts the tokens back in their original order;
+ * this applies it on the device.
+ *
+ *   dst  [n, row_bytes], src [n_src, row_bytes]: device, 16-byte aligned,
+ *        row_bytes a positive multiple of 16; dst and src must not overlap.
+ *   idx  device int64 [n].  An index outside [0, n_src) gives a zero row
+ *        (it is never dereferenced).
+ * ---------------------------------------------------------------------- */
+int32_t cp_gather_rows(void* dst, const void* src, const int64_t* idx, int64_t n, int64_t n_src,
+                       int64_t row_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * lse_merge -- combine n partial (O, LSE) results of the same rows.
  * [CP] DCP section (output and LSE combined to update the result);
  * [RA] memory-wall excerpt (running max and running sum).

@@ -27,7 +27,8 @@ ABI_VERSION = 2
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
             "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
-            "ring_attn_step_jobs", "split_kv_decode_paged")
+            "ring_attn_step_jobs", "split_kv_decode_paged", "ring_attn_step_varlen",
+            "cp_gather_rows")
 
 
 class RingAttnError(RuntimeError):
@@ -68,6 +69,11 @@ _lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i3
 _lib.split_kv_decode_paged.restype = _i32
 _lib.split_kv_decode_paged.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                        _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+_lib.ring_attn_step_varlen.restype = _i32
+_lib.ring_attn_step_varlen.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32,
+                                       _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]
+_lib.cp_gather_rows.restype = _i32
+_lib.cp_gather_rows.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.ring_stage_copy.restype = _i32
 _lib.ring_stage_copy.argtypes = [_vp, _vp, _vp, _i32, _vp]
 
@@ -375,6 +381,58 @@ def split_kv_decode_paged(q, k_pool, v_pool, block_tables, shard_lens, scale=Non
     return o_parts, lse_parts
 
 
+def ring_attn_step_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, q_pos0, k_pos0, o=None, lse=None,
+                          causal=True, scale=None, accumulate=False, stream=None):
+    """One ring step for packed requests: q [Tq,Hq,Dqk], k [Tk,Hkv,Dqk], v [Tk,Hkv,Dv] (bf16);
+    cu_seqlens_* / *_pos0 are host int64 sequences (per request).  Returns (o, lse) with
+    o [Tq,Hq,Dv] and lse [Tq,Hq] float32 (written, or LSE-merged when accumulate)."""
+    torch = _torch()
+    Tq, Hq, Dqk = q.shape
+    Tk, Hkv, Dk = k.shape
+    Dv = v.shape[2]
+    if Dk != Dqk or tuple(v.shape[:2]) != (Tk, Hkv):
+        raise ValueError("q / k / v shapes do not agree")
+    cq = np.ascontiguousarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.ascontiguousarray(cu_seqlens_k, dtype=np.int64)
+    pq = np.ascontiguousarray(q_pos0, dtype=np.int64)
+    pk = np.ascontiguousarray(k_pos0, dtype=np.int64)
+    n = pq.size
+    if cq.size != n + 1 or ck.size != n + 1 or pk.size != n:
+        raise ValueError("cu_seqlens need n_req + 1 entries, positions n_req")
+    if cq[-1] > Tq or ck[-1] > Tk:
+        raise ValueError("cu_seqlens run past the packed tensors")
+    if o is None:
+        o = torch.empty((Tq, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    if tuple(o.shape) != (Tq, Hq, Dv) or tuple(lse.shape) != (Tq, Hq):
+        raise ValueError("o / lse shapes do not agree with q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    _check(_lib.ring_attn_step_varlen(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q),
+                                      n, _np_ptr(cq), _np_ptr(ck), _np_ptr(pq), _np_ptr(pk), Hq, Hkv,
+                                      Dqk, Dv, CP_MASK_CAUSAL if causal else CP_MASK_NONE, float(scale),
+                                      1 if accumulate else 0, _dev_ptr(o, "o"), _dev_ptr(lse, "lse"),
+                                      _stream_handle(stream)), "ring_attn_step_varlen")
+    return o, lse
+
+
+def gather_rows(src, idx, dst=None, stream=None):
+    """dst[i] = src[idx[i]] along dim 0 on the device (idx: int64 GPU tensor)."""
+    torch = _torch()
+    n = idx.numel()
+    if idx.dtype != torch.int64:
+        raise ValueError("idx must be int64")
+    if dst is None:
+        dst = torch.empty((n, *src.shape[1:]), dtype=src.dtype, device=src.device)
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else dst[0].numel() * dst.element_size()
+    if tuple(dst.shape[1:]) != tuple(src.shape[1:]) or dst.shape[0] != n or dst.dtype != src.dtype:
+        raise ValueError("dst must be [len(idx), *src.shape[1:]] of src's dtype")
+    _check(_lib.cp_gather_rows(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), _dev_ptr(idx, "idx"), n,
+                               src.shape[0], row_bytes, _stream_handle(stream)), "cp_gather_rows")
+    return dst
+
+
 def stage_copy(pairs, stream=None):
     """Copy each (dst, src) pair of equally sized contiguous GPU tensors in one launch."""
     n = len(pairs)
@@ -394,6 +452,7 @@ from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E
 
 __all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "ring_attn_step_jobs",
            "lse_merge", "stage_copy",
-           "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged", "ZigzagRing", "segmented_prefill",
+           "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged",
+           "ring_attn_step_varlen", "gather_rows", "ZigzagRing", "segmented_prefill",
            "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
            "last_error"]

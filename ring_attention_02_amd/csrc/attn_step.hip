@@ -71,6 +71,17 @@ struct QJob {
   int32_t accumulate, n_seg;
   KvSeg seg[kMaxSegs];
 };
+// Packed variable-length requests (one launch covers up to kMaxReq): request
+// r's queries are rows [q_start, q_start + q_len) of the packed Q / O / LSE
+// (whose base pointers are job 0's) at absolute positions q_pos0.., its keys
+// rows [k_start, k_start + k_len) of the packed K / V (job 0's segment 0) at
+// positions k_pos0..; attention never crosses requests.
+constexpr int kMaxReq = 64;
+struct ReqDesc {
+  int32_t q_start, q_len, k_start, k_len;
+  int64_t q_pos0, k_pos0;
+};
+
 // Byte ranges the launch forwards around the ring while it computes, in
 // 16-byte units; fwd_end holds inclusive prefix sums (entries past n_fwd
 // repeat the total) and each workgroup moves fwd_per_wg consecutive units.
@@ -92,6 +103,22 @@ struct JobArgs {
   int32_t causal, reverse_q;
   float scale, scale_log2;
 };
+struct VarlenArgs {
+  JobArgs base;
+  ReqDesc req[kMaxReq];
+  int32_t n_req;
+};
+template <bool VARLEN>
+struct KernelArgs {
+  using type = JobArgs;
+};
+template <>
+struct KernelArgs<true> {
+  using type = VarlenArgs;
+};
+__device__ __forceinline__ const JobArgs& base_args(const JobArgs& x) { return x; }
+__device__ __forceinline__ const JobArgs& base_args(const VarlenArgs& x) { return x.base; }
+
 
 // Folds a block partial (o_blk, lse_blk) into the running (o, lse) of one
 // row.  Returns the merged LSE and the weights of the old and the new part.
@@ -215,9 +242,11 @@ struct FwdSlice {
 // tiles of the same 128 query rows while waves 0-3 sweep the even ones, and
 // the two softmax states are merged through LDS at the end.  This keeps two
 // waves per SIMD even when a launch has only one workgroup per CU.
-template <int DQK, int DV, int SPLIT, bool PAIRED>
-__global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(JobArgs a) {
+template <int DQK, int DV, int SPLIT, bool PAIRED, bool VARLEN>
+__global__ void __launch_bounds__(kThreads * SPLIT, 2)
+attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+  const JobArgs& a = base_args(args);
   using C = Bf16Cfg<DQK, DV>;
   // K stages of both halves, then V stages of both halves.
   __shared__ __attribute__((aligned(16))) uint16_t smem[SPLIT * 2 * (C::KTILE + C::VTILE)];
@@ -252,6 +281,13 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
     jb0 = 0;
     qt0 = logical % a.n_qtiles;
     rest = logical / a.n_qtiles;
+  } else if constexpr (VARLEN) {
+    // query tile fastest, then request (jb0 names the request here)
+    qt0 = logical % a.n_qtiles;
+    rest = logical / a.n_qtiles;
+    jb0 = rest % args.n_req;
+    rest /= args.n_req;
+    if (a.reverse_q) qt0 = a.n_qtiles - 1 - qt0;
   } else {
     jb0 = logical % a.n_jobs;
     rest = logical / a.n_jobs;
@@ -268,16 +304,57 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   if (item > 0) __syncthreads();   // the previous item is done with the LDS stages
   const int jb = item == 0 ? jb0 : 1;
   const int qt = item == 0 ? qt0 : a.n_qtiles - 1 - qt0;
-  const QJob& job = a.job[jb];
+  const QJob& job = a.job[VARLEN ? 0 : jb];
+  // The job's fields: its own, or a packed request's slice of job 0's
+  // buffers (one segment).  Read where they are used (no copies held live).
+  auto j_sq = [&]() -> int64_t {
+    if constexpr (VARLEN) return args.req[jb].q_len;
+    else return a.sq;
+  };
+  auto j_qpos0 = [&]() -> int64_t {
+    if constexpr (VARLEN) return args.req[jb].q_pos0;
+    else return job.q_pos0;
+  };
+  auto j_o = [&]() -> float* {
+    if constexpr (VARLEN) return job.o + static_cast<int64_t>(args.req[jb].q_start) * a.hq * DV;
+    else return job.o;
+  };
+  auto j_lse = [&]() -> float* {
+    if constexpr (VARLEN) return job.lse + static_cast<int64_t>(args.req[jb].q_start) * a.hq;
+    else return job.lse;
+  };
+  auto j_nseg = [&]() -> int {
+    if constexpr (VARLEN) return 1;
+    else return job.n_seg;
+  };
+  auto seg_base = [&](int sg, bool is_k) -> const uint16_t* {
+    if constexpr (VARLEN)
+      return static_cast<const uint16_t*>(is_k ? job.seg[0].k : job.seg[0].v) +
+             static_cast<int64_t>(args.req[jb].k_start) * a.hkv * (is_k ? DQK : DV);
+    else
+      return static_cast<const uint16_t*>(is_k ? job.seg[sg].k : job.seg[sg].v);
+  };
+  auto seg_sk = [&](int sg) -> int64_t {
+    if constexpr (VARLEN) return args.req[jb].k_len;
+    else return job.seg[sg].sk;
+  };
+  auto seg_kpos0 = [&](int sg) -> int64_t {
+    if constexpr (VARLEN) return args.req[jb].k_pos0;
+    else return job.seg[sg].k_pos0;
+  };
+  const int64_t sq = j_sq();
+  if (VARLEN && static_cast<int64_t>(qt) * kBM >= sq) continue;   // past this request's queries
+  const uint16_t* jq = static_cast<const uint16_t*>(job.q);
+  if constexpr (VARLEN) jq += static_cast<int64_t>(args.req[jb].q_start) * a.hq * DQK;
 
-  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(job.q);
+  const uint16_t* __restrict__ qg = jq;
 
   const int64_t q_first = static_cast<int64_t>(qt) * kBM;
-  const int64_t q_last = min(a.sq, q_first + kBM) - 1;  // last valid local row of the WG
+  const int64_t q_last = min(sq, q_first + kBM) - 1;  // last valid local row of the WG
   const int64_t wq0 = q_first + wave * 32;              // first row of this wave
   const int64_t my_row = wq0 + col;
-  const bool row_valid = my_row < a.sq;
-  const int64_t qpos = job.q_pos0 + my_row;
+  const bool row_valid = my_row < sq;
+  const int64_t qpos = j_qpos0() + my_row;
 
   // The job's segments, each with the number of its tiles that some row of
   // this workgroup can see; the sweep walks them segment after segment
@@ -285,11 +362,10 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   // from the argument block (uniform scalar loads) only when the sweep
   // enters it, so no segment state occupies registers in between.
   auto seg_tiles = [&](int sg) -> int {
-    if (sg >= job.n_seg) return 0;
-    const KvSeg& x = job.seg[sg];
-    int64_t nkeys = x.sk;
+    if (sg >= j_nseg()) return 0;
+    int64_t nkeys = seg_sk(sg);
     if (a.causal) {
-      const int64_t lim = job.q_pos0 + q_last - x.k_pos0 + 1;
+      const int64_t lim = j_qpos0() + q_last - seg_kpos0(sg) + 1;
       nkeys = lim < 0 ? 0 : (lim < nkeys ? lim : nkeys);
     }
     return static_cast<int>((nkeys + kBN - 1) / kBN);
@@ -309,7 +385,7 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   // Q^T fragment (B operand): for step c the lane holds Q[row][16c + 8hh .. +7].
   bf16x8 qf[C::QC];
   {
-    const uint16_t* qp = qg + ((static_cast<int64_t>(b) * a.sq + (row_valid ? my_row : 0)) * a.hq + h) * DQK;
+    const uint16_t* qp = qg + ((static_cast<int64_t>(b) * sq + (row_valid ? my_row : 0)) * a.hq + h) * DQK;
 #pragma unroll
     for (int c = 0; c < C::QC; ++c) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * c + 8 * hh);
@@ -359,14 +435,13 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   };
   auto seek = [&](DmaCursor& c, int vt, bool is_k) {
     advance(c.sg, c.start, c.end, vt);
-    const KvSeg& x = job.seg[c.sg];
+    const int64_t sk = seg_sk(c.sg);
     const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
     const int width = is_k ? DQK : DV;
-    const uint16_t* base = static_cast<const uint16_t*>(is_k ? x.k : x.v) +
-                           (static_cast<int64_t>(b) * x.sk * a.hkv + kvh) * width;
+    const uint16_t* base = seg_base(c.sg, is_k) + (static_cast<int64_t>(b) * sk * a.hkv + kvh) * width;
     const int64_t key0 = static_cast<int64_t>(vt - c.start) * kBN;
     // bytes from the base tile to the end of key sk-1's row of this head
-    const int64_t valid = ((x.sk - 1 - key0) * row_elems + width) * 2;
+    const int64_t valid = ((sk - 1 - key0) * row_elems + width) * 2;
     const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
     c.base_vt = vt;
     c.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
@@ -451,12 +526,12 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   auto mask_tile = [&](int vt, f32x16* s) {
     if (vt >= mcur.end) {
       advance(mcur.sg, mcur.start, mcur.end, vt);
-      mcur.sk = job.seg[mcur.sg].sk;
-      mcur.k_pos0 = job.seg[mcur.sg].k_pos0;
+      mcur.sk = seg_sk(mcur.sg);
+      mcur.k_pos0 = seg_kpos0(mcur.sg);
       int64_t from = mcur.sk / kBN;                       // the partial last tile, if any
       if (a.causal) {
         // key0 + kBN - 1 > q_pos0 + wq0 - k_pos0  <=>  key0 >= that - kBN + 2
-        const int64_t d = job.q_pos0 + wq0 - mcur.k_pos0 - kBN + 2;
+        const int64_t d = j_qpos0() + wq0 - mcur.k_pos0 - kBN + 2;
         const int64_t tc = d <= 0 ? 0 : (d + kBN - 1) / kBN;
         from = min(from, tc);
       }
@@ -609,10 +684,10 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
   const bool has = m_run != kNegInf && l_tot > 0.f;
   const float inv = has ? 1.f / l_tot : 0.f;
   const float lse_blk = has ? m_run * a.scale + fast_log2(l_tot) * kLn2 : kNegInf;
-  const int64_t orow = (static_cast<int64_t>(b) * a.sq + my_row) * a.hq + h;
-  float* op = job.o + orow * DV;
+  const int64_t orow = (static_cast<int64_t>(b) * sq + my_row) * a.hq + h;
+  float* op = j_o() + orow * DV;
   float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
-  if (job.accumulate) lse_out = merge_weights(job.lse[orow], lse_blk, &w_old, &w_blk);
+  if (job.accumulate) lse_out = merge_weights(j_lse()[orow], lse_blk, &w_old, &w_blk);
   const float wb = w_blk * inv;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
@@ -627,7 +702,7 @@ __global__ void __launch_bounds__(kThreads * SPLIT, 2) attn_step_bf16_kernel(Job
       }
       *reinterpret_cast<f32x4*>(op + dv0) = val;
     }
-  if (hh == 0) job.lse[orow] = lse_out;
+  if (hh == 0) j_lse()[orow] = lse_out;
   }
   }   // work items
 #endif
@@ -800,18 +875,47 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
       if (args.paired)
-        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true>), grid, dim3(2 * kThreads), 0, stream, args);
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true, false>), grid, dim3(2 * kThreads), 0,
+                           stream, args);
       else
-        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false>), grid, dim3(2 * kThreads), 0, stream, args);
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, false>), grid, dim3(2 * kThreads), 0,
+                           stream, args);
       const hipError_t err = hipGetLastError();
       RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
       return CP_OK;
     }
   }
   RA_CHECK(!args.paired, CP_EUNSUPPORTED, "ring_attn_step: paired launch needs the 8-wave variant");
-  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false>), grid, dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
+  return CP_OK;
+}
+
+// Varlen launch: every (query tile up to the longest request, request,
+// head); tiles past a request's end exit at once.
+template <int DQK, int DV>
+int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
+  const int64_t n_qtiles = (max_q + kBM - 1) / kBM;
+  const int64_t total = n_qtiles * args.n_req * args.base.hq;
+  RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
+           "ring_attn_step_varlen: %lld workgroups exceed the grid limit", static_cast<long long>(total));
+  if (total == 0) return CP_OK;
+  args.base.n_qtiles = static_cast<int32_t>(n_qtiles);
+  args.base.total_wgs = static_cast<int32_t>(total);
+  const dim3 grid(static_cast<unsigned>(total));
+  if constexpr (DQK <= 128) {
+    if (total < 2 * static_cast<int64_t>(device_cus())) {
+      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, true>), grid, dim3(2 * kThreads), 0,
+                         stream, args);
+      const hipError_t err = hipGetLastError();
+      RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));
+      return CP_OK;
+    }
+  }
+  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, true>), grid, dim3(kThreads), 0, stream, args);
+  const hipError_t err = hipGetLastError();
+  RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));
   return CP_OK;
 }
 
@@ -1069,4 +1173,73 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
   ja.scale = scale; ja.scale_log2 = scale * kLog2e;
   const int32_t rc = launch_bf16_any(d_qk, ja, batch, static_cast<hipStream_t>(stream));
   return rc == CP_OK ? ok() : rc;
+}
+
+extern "C" int32_t ring_attn_step_varlen(const void* q, const void* k, const void* v, int32_t dtype,
+                                         int32_t n_req, const int64_t* cu_seqlens_q,
+                                         const int64_t* cu_seqlens_k, const int64_t* q_pos0,
+                                         const int64_t* k_pos0, int32_t hq, int32_t hkv, int32_t d_qk,
+                                         int32_t d_v, int32_t mask, float scale, int32_t accumulate,
+                                         float* o, float* lse, void* stream) {
+  using namespace ringattn;
+  RA_CHECK(dtype == CP_BF16 || dtype == CP_F32, CP_EDTYPE, "ring_attn_step_varlen: dtype=%d", dtype);
+  RA_CHECK(dtype == CP_BF16, CP_EUNSUPPORTED, "ring_attn_step_varlen: only bf16 inputs");
+  RA_CHECK(n_req >= 0, CP_EINVAL, "ring_attn_step_varlen: n_req=%d < 0", n_req);
+  RA_CHECK(hq > 0 && hkv > 0 && hq % hkv == 0, CP_EINVAL,
+           "ring_attn_step_varlen: hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  RA_CHECK(mask == CP_MASK_NONE || mask == CP_MASK_CAUSAL, CP_EINVAL, "ring_attn_step_varlen: mask=%d", mask);
+  RA_CHECK(scale > 0.f && scale < __builtin_huge_valf(), CP_EINVAL,
+           "ring_attn_step_varlen: scale must be positive and finite");
+  RA_CHECK(accumulate == 0 || accumulate == 1, CP_EINVAL, "ring_attn_step_varlen: accumulate=%d", accumulate);
+  RA_CHECK(head_dims_ok(d_qk, d_v), CP_EUNSUPPORTED,
+           "ring_attn_step_varlen: (d_qk, d_v) = (%d, %d) not supported", d_qk, d_v);
+  if (n_req == 0) return ok();
+  RA_CHECK(cu_seqlens_q && cu_seqlens_k && q_pos0 && k_pos0, CP_EINVAL,
+           "ring_attn_step_varlen: NULL host array");
+  int64_t max_q = 0;
+  for (int32_t r = 0; r < n_req; ++r) {
+    const int64_t lq = cu_seqlens_q[r + 1] - cu_seqlens_q[r], lk = cu_seqlens_k[r + 1] - cu_seqlens_k[r];
+    RA_CHECK(cu_seqlens_q[r] >= 0 && cu_seqlens_k[r] >= 0 && lq >= 0 && lk >= 0, CP_EINVAL,
+             "ring_attn_step_varlen: cu_seqlens must start >= 0 and not decrease (request %d)", r);
+    max_q = std::max(max_q, lq);
+  }
+  const int64_t total_q = cu_seqlens_q[n_req], total_k = cu_seqlens_k[n_req];
+  RA_CHECK(total_q < (int64_t{1} << 31) && total_k < (int64_t{1} << 31), CP_EUNSUPPORTED,
+           "ring_attn_step_varlen: packed lengths must stay below 2^31 tokens");
+  if (total_q == 0) return ok();
+  RA_CHECK(q && o && lse && aligned16(q) && aligned16(o) && (total_k == 0 || (k && v && aligned16(k) && aligned16(v))),
+           CP_EINVAL, "ring_attn_step_varlen: NULL or misaligned device pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Requests go kMaxReq per launch.
+  for (int32_t r0 = 0; r0 < n_req; r0 += kMaxReq) {
+    VarlenArgs va{};
+    JobArgs& ja = va.base;
+    ja.job[0].q = q; ja.job[0].o = o; ja.job[0].lse = lse; ja.job[0].accumulate = accumulate;
+    ja.job[0].n_seg = 1;
+    ja.job[0].seg[0] = KvSeg{k, v, 0, 0};
+    ja.n_jobs = 1; ja.sq = 0; ja.hq = hq; ja.hkv = hkv; ja.group = hq / hkv;
+    ja.causal = mask == CP_MASK_CAUSAL;
+    ja.reverse_q = ja.causal;   // the longest query tiles of causal requests first
+    ja.scale = scale; ja.scale_log2 = scale * kLog2e;
+    int64_t group_max_q = 0;
+    const int32_t n = std::min(kMaxReq, n_req - r0);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t r = r0 + i;
+      ReqDesc& d = va.req[i];
+      d.q_start = static_cast<int32_t>(cu_seqlens_q[r]);
+      d.q_len = static_cast<int32_t>(cu_seqlens_q[r + 1] - cu_seqlens_q[r]);
+      d.k_start = static_cast<int32_t>(cu_seqlens_k[r]);
+      d.k_len = static_cast<int32_t>(cu_seqlens_k[r + 1] - cu_seqlens_k[r]);
+      d.q_pos0 = q_pos0[r];
+      d.k_pos0 = k_pos0[r];
+      group_max_q = std::max<int64_t>(group_max_q, d.q_len);
+    }
+    va.n_req = n;
+    int32_t rc;
+    if (d_qk == 64) rc = launch_bf16_varlen<64, 64>(va, group_max_q, st);
+    else if (d_qk == 128) rc = launch_bf16_varlen<128, 128>(va, group_max_q, st);
+    else rc = launch_bf16_varlen<192, 128>(va, group_max_q, st);
+    if (rc != CP_OK) return rc;
+  }
+  return ok();
 }

@@ -70,3 +70,52 @@ extern "C" int32_t ring_stage_copy(void* const* dsts, const void* const* srcs,
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_stage_copy: launch failed: %s", hipGetErrorString(err));
   return ok();
 }
+
+namespace ringattn {
+namespace {
+
+// One row per group of threads: each thread moves 16-byte units of row i.
+__global__ void __launch_bounds__(kStageThreads) gather_rows_kernel(u32x4* __restrict__ dst,
+                                                                   const u32x4* __restrict__ src,
+                                                                   const int64_t* __restrict__ idx,
+                                                                   int64_t n, int64_t n_src,
+                                                                   int64_t units_per_row) {
+  const int64_t total = n * units_per_row;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStageThreads;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; u < total; u += stride) {
+    const int64_t row = u / units_per_row, col = u - row * units_per_row;
+    const int64_t from = idx[row];
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (from >= 0 && from < n_src) x = src[from * units_per_row + col];
+    dst[u] = x;
+  }
+}
+
+}  // namespace
+}  // namespace ringattn
+
+extern "C" int32_t cp_gather_rows(void* dst, const void* src, const int64_t* idx, int64_t n,
+                                  int64_t n_src, int64_t row_bytes, void* stream) {
+  using namespace ringattn;
+  RA_CHECK(n >= 0 && n_src >= 0, CP_EINVAL, "cp_gather_rows: negative row count");
+  RA_CHECK(row_bytes > 0 && row_bytes % 16 == 0, CP_EINVAL,
+           "cp_gather_rows: row_bytes=%lld must be a positive multiple of 16",
+           static_cast<long long>(row_bytes));
+  if (n == 0) return ok();
+  RA_CHECK(dst && idx && (n_src == 0 || src), CP_EINVAL, "cp_gather_rows: NULL pointer");
+  RA_CHECK((reinterpret_cast<uintptr_t>(dst) & 15u) == 0 && (reinterpret_cast<uintptr_t>(src) & 15u) == 0,
+           CP_EINVAL, "cp_gather_rows: dst / src must be 16-byte aligned");
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), s0 = reinterpret_cast<uintptr_t>(src);
+  RA_CHECK(n_src == 0 || d0 >= s0 + static_cast<uintptr_t>(n_src * row_bytes) ||
+               s0 >= d0 + static_cast<uintptr_t>(n * row_bytes),
+           CP_EINVAL, "cp_gather_rows: dst and src overlap");
+  const int64_t units = row_bytes / 16;
+  const int64_t want = (n * units + kStageThreads * 4 - 1) / (kStageThreads * 4);
+  const unsigned blocks = static_cast<unsigned>(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kStageThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
+                     static_cast<const u32x4*>(src), idx, n, n_src, units);
+  const hipError_t err = hipGetLastError();
+  RA_CHECK(err == hipSuccess, CP_EHIP, "cp_gather_rows: launch failed: %s", hipGetErrorString(err));
+  return ok();
+}

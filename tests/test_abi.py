@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 15, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
@@ -234,3 +234,36 @@ def test_decode_paged_validates_before_launch(ra):
     assert call(lens=None) == ra.CP_EINVAL
     assert call(d=64) == ra.CP_EUNSUPPORTED
     assert call(batch=0) == ra.CP_OK          # nothing to do, nothing launched
+
+
+def test_varlen_and_gather_validate_before_launch(ra):
+    import numpy as np
+    lib = ra.lib()
+    fake = ctypes.c_void_p(1 << 20)
+
+    def arr(*x):
+        a = np.asarray(x, dtype=np.int64)
+        return a, ctypes.c_void_p(a.ctypes.data)
+
+    def call(cq, ck, pq, pk, n=None, d=128, dtype=0, acc=0, mask=1):
+        n = len(pq[0]) if n is None else n
+        return lib.ring_attn_step_varlen(fake, fake, fake, dtype, n, cq[1], ck[1], pq[1], pk[1], 4, 2,
+                                         d, d, mask, 0.1, acc, fake, fake, None)
+    cq, ck, pq, pk = arr(0, 10, 30), arr(0, 5, 40), arr(0, 100), arr(0, 90)
+    assert call(arr(0, 10, 5), ck, pq, pk) == ra.CP_EINVAL and "not decrease" in ra.last_error()
+    assert call(cq, arr(-1, 5, 40), pq, pk) == ra.CP_EINVAL
+    assert call(cq, ck, pq, pk, dtype=1) == ra.CP_EUNSUPPORTED
+    assert call(cq, ck, pq, pk, d=96) == ra.CP_EUNSUPPORTED
+    assert call(cq, ck, pq, pk, acc=3) == ra.CP_EINVAL
+    assert call(cq, ck, pq, pk, mask=5) == ra.CP_EINVAL
+    assert call(cq, ck, pq, pk, n=-1) == ra.CP_EINVAL
+    assert call(arr(0, 0, 0), ck, pq, pk) == ra.CP_OK            # no queries: nothing launched
+    assert lib.ring_attn_step_varlen(fake, fake, fake, 0, 2, None, ck[1], pq[1], pk[1], 4, 2, 128, 128,
+                                     1, 0.1, 0, fake, fake, None) == ra.CP_EINVAL
+    # gather: sizes, alignment, overlap
+    g = lib.cp_gather_rows
+    assert g(fake, fake, fake, 4, 4, 24, None) == ra.CP_EINVAL        # row not a multiple of 16
+    assert g(fake, fake, fake, -1, 4, 32, None) == ra.CP_EINVAL
+    assert g(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 24), fake, 4, 4, 32, None) == ra.CP_EINVAL
+    assert g(fake, ctypes.c_void_p((1 << 20) + 64), fake, 4, 4, 32, None) == ra.CP_EINVAL   # overlap
+    assert g(fake, fake, fake, 0, 4, 32, None) == ra.CP_OK

@@ -150,8 +150,9 @@ def test_zigzag_all_ranks_restore(ra):
         ring.run(q_local, o, lse)
         gathered_o.append(o)
         gathered_l.append(lse)
-    o = torch.cat(gathered_o, 1)[:, torch.from_numpy(restore).cuda()]
-    lse = torch.cat(gathered_l, 1)[:, torch.from_numpy(restore).cuda()]
+    restore_t = torch.from_numpy(restore).cuda()          # applied on the device
+    o = ra.gather_rows(torch.cat(gathered_o, 1)[0], restore_t)[None]
+    lse = ra.gather_rows(torch.cat(gathered_l, 1)[0], restore_t)[None]
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, causal=True)
     compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "zigzag all ranks")
@@ -456,3 +457,77 @@ def test_split_kv_decode_paged_splits_and_small_blocks(ra):
 def test_split_kv_decode_paged_entry_outside_pool(ra):
     say("paged decode: one table entry outside the pool is an empty block")
     _decode_paged_case(ra, 46, 2, [2048, 1000], 4, 8, 1, 64, 16, spare_blocks=3, drop=(1, 0, 2))
+
+
+
+def test_gather_rows_out_of_range_is_zero(ra):
+    src = torch.randn((50, 3, 8), device="cuda")
+    idx = torch.tensor([4, -1, 49, 50, 0, 4], dtype=torch.int64, device="cuda")
+    out = ra.gather_rows(src, idx)
+    torch.cuda.synchronize()
+    for i, j in enumerate([4, -1, 49, 50, 0, 4]):
+        want = src[j] if 0 <= j < 50 else torch.zeros_like(src[0])
+        assert torch.equal(out[i], want)
+
+
+# (q_len, k_len, q_pos0, k_pos0) of packed requests: self-causal, single
+# token, no queries, chunk tail over a long prefix, no keys, all keys later
+# (nothing visible), ragged tails past the tile size.
+VARLEN_REQS = [(300, 300, 0, 0), (1, 1, 7, 7), (0, 50, 0, 0), (130, 1131, 1001, 0), (64, 0, 0, 0),
+               (257, 100, 0, 500), (129, 200, 3000, 2900)]
+
+
+def _varlen_case(ra, cfg, reqs, hq, hkv, dqk, dv, causal=True, split_keys=False):
+    n = len(reqs)
+    cq = np.concatenate([[0], np.cumsum([r[0] for r in reqs])]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum([r[1] for r in reqs])]).astype(np.int64)
+    pq = np.array([r[2] for r in reqs], dtype=np.int64)
+    pk = np.array([r[3] for r in reqs], dtype=np.int64)
+    q, q64 = tensor(cfg, 1, 0, (int(cq[-1]), hq, dqk), torch.bfloat16)
+    k, k64 = tensor(cfg, 2, 0, (int(ck[-1]), hkv, dqk), torch.bfloat16)
+    v, v64 = tensor(cfg, 3, 0, (int(ck[-1]), hkv, dv), torch.bfloat16)
+    if not split_keys:
+        o, lse = ra.ring_attn_step_varlen(q, k, v, cq, ck, pq, pk, causal=causal)
+    else:
+        # first half of every request's keys, then the second half merged in
+        half = np.array([r[1] // 2 for r in reqs], dtype=np.int64)
+        ck1 = np.concatenate([[0], np.cumsum(half)])
+        ck2 = np.concatenate([[0], np.cumsum([r[1] - h for r, h in zip(reqs, half)])])
+        sel1 = np.concatenate([np.arange(ck[i], ck[i] + half[i]) for i in range(n)]).astype(np.int64)
+        sel2 = np.concatenate([np.arange(ck[i] + half[i], ck[i + 1]) for i in range(n)]).astype(np.int64)
+        k1, v1 = k[torch.from_numpy(sel1).cuda()].contiguous(), v[torch.from_numpy(sel1).cuda()].contiguous()
+        k2, v2 = k[torch.from_numpy(sel2).cuda()].contiguous(), v[torch.from_numpy(sel2).cuda()].contiguous()
+        o, lse = ra.ring_attn_step_varlen(q, k1, v1, cq, ck1, pq, pk, causal=causal)
+        ra.ring_attn_step_varlen(q, k2, v2, cq, ck2, pq, pk + half, o=o, lse=lse, causal=causal,
+                                 accumulate=True)
+    torch.cuda.synchronize()
+    o64, l64 = host64(o), host64(lse)
+    for i, (lq, lk, q0, k0) in enumerate(reqs):
+        if lq == 0:
+            continue
+        rows = slice(int(cq[i]), int(cq[i + 1]))
+        keys = slice(int(ck[i]), int(ck[i + 1]))
+        if lk:
+            ro, rl = oracle.attention_ref(q64[None, rows], k64[None, keys], v64[None, keys],
+                                          q0 + np.arange(lq), k0 + np.arange(lk), causal)
+        else:
+            ro, rl = np.zeros((1, lq, hq, dv)), np.full((1, lq, hq), -np.inf)
+        compare(o64[None, rows], l64[None, rows], ro, rl, BF16_O, BF16_LSE, f"varlen request {i}")
+
+
+@pytest.mark.parametrize("dqk,dv,hq,hkv", [(128, 128, 4, 2), (64, 64, 2, 2), (192, 128, 2, 1)])
+def test_varlen_packed_requests(ra, dqk, dv, hq, hkv):
+    say(f"varlen: {len(VARLEN_REQS)} packed requests, d {dqk}/{dv}")
+    _varlen_case(ra, 61, VARLEN_REQS, hq, hkv, dqk, dv)
+
+
+def test_varlen_noncausal_and_accumulate(ra):
+    _varlen_case(ra, 62, VARLEN_REQS, 4, 1, 128, 128, causal=False)
+    _varlen_case(ra, 63, VARLEN_REQS, 4, 2, 128, 128, split_keys=True)
+
+
+def test_varlen_more_requests_than_one_launch(ra):
+    rng = np.random.default_rng(64)
+    reqs = [(int(rng.integers(0, 90)), int(rng.integers(0, 150)), int(rng.integers(0, 200)),
+             int(rng.integers(0, 200))) for _ in range(150)]
+    _varlen_case(ra, 64, reqs, 2, 1, 128, 128)
