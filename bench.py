@@ -16,7 +16,8 @@ heads x (2 d_qk + 2 d_v) per sweep / time per sweep.
 Also reported in the same line (unless --primary-only): the long zigzag
 prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
 (GB/s against HBM), the same decode over paged caches read through block
-tables, segmented chunked prefill (MLA shape) and a standalone LSE merge, each with the roofline of its dominant kernel, plus the CPU
+tables, segmented chunked prefill (MLA shape), a packed multi-request
+(varlen) prefill and a standalone LSE merge, each with the roofline of its dominant kernel, plus the CPU
 oracle timed on the host.
 """
 
@@ -252,6 +253,21 @@ def segmented_bench(steps, warmup):
                         achieved_tflops=achieved)
 
 
+def varlen_bench(steps, warmup):
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.varlen_setup()
+
+    def step():
+        ra.ring_attn_step_varlen(w["q"], w["k"], w["v"], w["cu"], w["cu"], w["pos"], w["pos"],
+                                 o=w["o"], lse=w["lse"], causal=True)
+
+    sec = time_steps(step, steps, warmup)
+    ms = kernel_launch_stats([step], max(2, min(steps, 10)))
+    return w, sec, dict(mean_launch_ms=ms, achieved_tflops=w["flops"] / (ms * 1e-3) / 1e12)
+
+
 def merge_bench(steps, warmup):
     import torch
     import ring_attention_02_amd as ra
@@ -383,6 +399,17 @@ def main():
                 "roofline": roofline_entry("mfma", l5["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
                 "mean_launch_ms": round(l5["mean_launch_ms"], 4)}
             del w5
+            torch.cuda.empty_cache()
+        if not only or "varlen" in only:
+            log("varlen: 16 packed requests (512..8192 tokens), self-causal, GQA 32/8, d 128")
+            w7, s7, l7 = varlen_bench(max(3, min(args.steps, 10)), 2)
+            sec["varlen_packed_prefill"] = {
+                "value": round(w7["flops"] / s7 / 1e12, 3), "unit": "TFLOP/s",
+                "ms_per_step": round(s7 * 1e3, 4), "flops_per_step": w7["flops"],
+                "tokens": int(w7["cu"][-1]),
+                "roofline": roofline_entry("mfma", l7["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+                "mean_launch_ms": round(l7["mean_launch_ms"], 4)}
+            del w7
             torch.cuda.empty_cache()
         if not only or "merge" in only:
             log("lse_merge: 2 partials x 8.4M rows x 128")

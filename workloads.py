@@ -173,3 +173,23 @@ def segmented_setup():
     pairs = causal_pairs(q0, sq, 0, skv)
     return dict(q=q, k=k, v=v, o=o, lse=lse, q_pos0=q0, segment=c["segment"], sq=sq, h=h,
                 dqk=dqk, dv=dv, skv=skv, pairs=pairs, flops=pairs * h * (2 * dqk + 2 * dv))
+
+
+def varlen_setup(n_req=16, hq=32, hkv=8, d=128, seed_cfg=6):
+    """Packed multi-request prefill: n_req requests whose lengths are a
+    seeded uniform draw in [512, 8192] tokens (multiples of 64), each
+    attending causally to itself; GQA 32/8, d 128, bf16 N(0, 1)."""
+    torch = _torch()
+    rng = np.random.default_rng(si.device_seed(seed_cfg, 0, 0))
+    lens = (rng.integers(512 // 64, 8192 // 64 + 1, size=n_req) * 64).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total = int(cu[-1])
+    q = si.device_normal(seed_cfg, Q_ID, 0, (total, hq, d), torch.bfloat16, "cuda")
+    k = si.device_normal(seed_cfg, K_ID, 0, (total, hkv, d), torch.bfloat16, "cuda")
+    v = si.device_normal(seed_cfg, V_ID, 0, (total, hkv, d), torch.bfloat16, "cuda")
+    o = torch.empty((total, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((total, hq), dtype=torch.float32, device="cuda")
+    pairs = int(sum(int(L) * (int(L) + 1) // 2 for L in lens))
+    zeros = np.zeros(n_req, dtype=np.int64)
+    return dict(q=q, k=k, v=v, o=o, lse=lse, cu=cu, pos=zeros, lens=lens, hq=hq, hkv=hkv, d=d,
+                pairs=pairs, flops=pairs * hq * 4 * d)
