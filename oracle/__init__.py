@@ -13,8 +13,9 @@ for a reader who checks it against the pages by eye:
   absolute-position causal mask, its log-sum-exp, the LSE merge of
   partials, and decode over a sequence-sharded KV cache.
 * ``index``      -- the head-tail (zigzag) partition and restore index, the
-  interleaved virtual-block slot mapping, the ring step schedule and the
-  full / diagonal / skip block classification.
+  interleaved virtual-block slot mapping, the ring step schedule, the
+  full / diagonal / skip block classification and the reorganisation index
+  of an all-gathered KV cache.
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against
 closed forms, brute force, worked examples derived from the pages' rules
@@ -24,10 +25,10 @@ closed forms, brute force, worked examples derived from the pages' rules
 from .attention import attention_ref, lse_merge_ref, decode_shards_ref
 from .index import (partition_ref, slot_mapping_ref, classify_ref,
                     ring_schedule_ref, zigzag_ring_chunks_ref,
-                    visible_pairs_ref, FULL, DIAG, SKIP)
+                    visible_pairs_ref, reorg_index_ref, FULL, DIAG, SKIP)
 
 __all__ = [
     "attention_ref", "lse_merge_ref", "decode_shards_ref",
     "partition_ref", "slot_mapping_ref", "classify_ref", "ring_schedule_ref",
-    "zigzag_ring_chunks_ref", "visible_pairs_ref", "FULL", "DIAG", "SKIP",
+    "zigzag_ring_chunks_ref", "visible_pairs_ref", "reorg_index_ref", "FULL", "DIAG", "SKIP",
 ]

@@ -32,7 +32,12 @@ Readings of what the pages leave open:
 * slot = block_table[virtual block] * block_size + in-block offset, with
   an identity block table by default; the device id is flat in
   [0, pcp_size*dcp_size);
-* a (query range, key range) pair with no (q, k) pair at all is SKIP.
+* a (query range, key range) pair with no (q, k) pair at all is SKIP;
+* (reorg_kvcache, MLA chunked prefill with all-gather KV in the same guide)
+  each device's KV buffer lists the requests in order, each request's tokens
+  at their local slots 0..n-1 (identity block table); the all-gather
+  concatenates the devices' buffers in device order; the reorganised KV
+  lists every request's tokens contiguously in their original order.
 """
 
 import numpy as np
@@ -153,3 +158,30 @@ def zigzag_ring_chunks_ref(rank, cp_size):
     parts s and 2*cp_size-1-s.
     """
     return [(s, 2 * cp_size - 1 - s) for s in ring_schedule_ref(rank, cp_size)]
+
+
+def reorg_index_ref(seq_lens, block_size, interleave, pcp_size, dcp_size):
+    """Rows of the all-gathered KV buffer, request by request, token by token.
+
+    MLA chunked prefill with all-gather KV (CP guide, PCP chunked-prefill
+    paragraph and MLA prefill note): the context KV is all-gathered, which
+    interleaves requests, and reorg_kvcache stores each request's KV
+    contiguously.  Simulated in that order: every device's buffer of
+    (request, token) entries by local slot, the all-gather, then each
+    request's tokens looked up in the gathered buffer.
+    Returns (src_idx int64[sum seq_lens], dev_lens int64[W, num_reqs]).
+    """
+    world = pcp_size * dcp_size
+    per_dev = [[] for _ in range(world)]
+    dev_lens = np.zeros((world, len(seq_lens)), dtype=np.int64)
+    for r, L in enumerate(seq_lens):
+        dev, slot = slot_mapping_ref(np.arange(int(L)), block_size, interleave, pcp_size, dcp_size)
+        for d in range(world):
+            mine = sorted((int(s_), x) for x, (dv, s_) in enumerate(zip(dev, slot)) if dv == d)
+            assert [s_ for s_, _ in mine] == list(range(len(mine))), "local slots must be 0..n-1"
+            per_dev[d].extend((r, x) for _, x in mine)
+            dev_lens[d, r] = len(mine)
+    gathered = [entry for d in range(world) for entry in per_dev[d]]      # the all-gather
+    where = {entry: row for row, entry in enumerate(gathered)}
+    src = [where[(r, x)] for r, L in enumerate(seq_lens) for x in range(int(L))]
+    return np.asarray(src, dtype=np.int64), dev_lens

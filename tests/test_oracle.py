@@ -384,3 +384,35 @@ def test_sharded_decode_merge_equals_unsharded():
     fo, fl = attention_ref(q[:, None], k, v)
     np.testing.assert_allclose(o, fo[:, 0], atol=TOL)
     np.testing.assert_allclose(lse, fl[:, 0], atol=TOL)
+
+
+def test_reorg_index_golden():
+    from oracle import reorg_index_ref
+    g = _load("reorg_examples.json")
+    for c in g["cases"]:
+        src, dev_lens = reorg_index_ref(c["seq_lens"], c["block_size"], c["interleave"],
+                                        c["pcp_size"], c["dcp_size"])
+        assert src.tolist() == c["src_idx"], c["derivation"]
+        assert dev_lens.tolist() == c["dev_lens"]
+
+
+@pytest.mark.parametrize("lens,bs,il,pcp,dcp", [([1000, 37, 0, 513], 16, 4, 2, 2), ([4096], 128, 16, 8, 1),
+                                                ([5, 9], 6, 3, 3, 1), ([300, 300], 32, 8, 1, 1)])
+def test_reorg_index_invariants(lens, bs, il, pcp, dcp):
+    from oracle import reorg_index_ref
+    src, dev_lens = reorg_index_ref(lens, bs, il, pcp, dcp)
+    n = sum(lens)
+    assert sorted(src.tolist()) == list(range(n))            # a permutation of the gathered rows
+    assert dev_lens.sum(0).tolist() == list(lens)            # every token on exactly one device
+    if pcp * dcp == 1:
+        assert src.tolist() == list(range(n))                # one device: already contiguous
+    # rebuild the gathered buffer from the placement alone and read it back
+    W = pcp * dcp
+    bufs = [[] for _ in range(W)]
+    for r, L in enumerate(lens):
+        dev, slot = slot_mapping_ref(np.arange(L), bs, il, pcp, dcp)
+        for d in range(W):
+            order = np.argsort(slot[dev == d], kind="stable")
+            bufs[d].extend(("tok", r, int(x)) for x in np.arange(L)[dev == d][order])
+    gathered = [e for d in range(W) for e in bufs[d]]
+    assert [gathered[i] for i in src] == [("tok", r, x) for r, L in enumerate(lens) for x in range(L)]
