@@ -17,7 +17,8 @@ Also reported in the same line (unless --primary-only): the long zigzag
 prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
 (GB/s against HBM), the same decode over paged caches read through block
 tables, segmented chunked prefill (MLA shape), a packed multi-request
-(varlen) prefill and a standalone LSE merge, each with the roofline of its dominant kernel, plus the CPU
+(varlen) prefill, the all-gather-KV reorganisation gather and a standalone
+LSE merge, each with the roofline of its dominant kernel, plus the CPU
 oracle timed on the host.
 """
 
@@ -268,6 +269,22 @@ def varlen_bench(steps, warmup):
     return w, sec, dict(mean_launch_ms=ms, achieved_tflops=w["flops"] / (ms * 1e-3) / 1e12)
 
 
+def reorg_bench(steps, warmup):
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.reorg_setup()
+    ok = torch.empty_like(w["gk"])
+    ov = torch.empty_like(w["gv"])
+
+    def step():
+        ra.gather_rows(w["gk"], w["idx"], dst=ok)
+        ra.gather_rows(w["gv"], w["idx"], dst=ov)
+
+    sec = time_steps(step, steps, warmup)
+    return w, sec
+
+
 def merge_bench(steps, warmup):
     import torch
     import ring_attention_02_amd as ra
@@ -410,6 +427,15 @@ def main():
                 "roofline": roofline_entry("mfma", l7["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
                 "mean_launch_ms": round(l7["mean_launch_ms"], 4)}
             del w7
+            torch.cuda.empty_cache()
+        if not only or "reorg" in only:
+            log("reorg_kvcache: all-gathered K/V of 135,168 tokens (4 requests, 8 devices) to request order")
+            w8, s8 = reorg_bench(max(3, min(args.steps, 10)), 2)
+            sec["reorg_kvcache_gather"] = {
+                "value": round(w8["bytes"] / s8 / 1e9, 1), "unit": "GB/s",
+                "ms_per_step": round(s8 * 1e3, 4), "bytes_per_step": w8["bytes"],
+                "roofline": roofline_entry("hbm", w8["bytes"] / s8 / 1e9, PEAK_HBM_GBS, "GB/s")}
+            del w8
             torch.cuda.empty_cache()
         if not only or "merge" in only:
             log("lse_merge: 2 partials x 8.4M rows x 128")

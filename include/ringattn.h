@@ -118,6 +118,29 @@ int32_t cp_slot_mapping(const int64_t* positions, int64_t n, int32_t block_size,
                         int32_t* device_out, int64_t* slot_out);
 
 /* ------------------------------------------------------------------------
+ * cp_reorg_index -- rows of an all-gathered KV buffer in request order.
+ * [CP] PCP chunked-prefill paragraph (AllGatherKV in the MLA backend) and
+ * the MLA prefill note: after the all-gather the KV of several requests is
+ * interleaved, and reorg_kvcache stores each request's KV contiguously.
+ *
+ * Gathered layout assumed: device d = 0..W-1 (W = pcp_size * dcp_size) in
+ * order, each holding requests 0..num_reqs-1 in order, each request's tokens
+ * at their local slots 0..n-1 (the slot mapping with an identity block
+ * table).  For request r and token x < seq_lens[r] (requests in order,
+ * tokens in original order), src_idx gets the gathered row of that token.
+ *
+ *   seq_lens  host int64 [num_reqs] context lengths.
+ *   src_idx   host int64 [sum seq_lens], or NULL to query the length.
+ *   src_len   host int64 out: sum of seq_lens (may be NULL).
+ *   dev_lens  host int64 [W * num_reqs] out, device-major: tokens of request
+ *             r on device d (may be NULL).
+ * CP_EINVAL as cp_slot_mapping for the sizes; negative lengths are invalid.
+ * ---------------------------------------------------------------------- */
+int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int32_t block_size,
+                       int32_t interleave, int32_t pcp_size, int32_t dcp_size, int64_t* src_idx,
+                       int64_t* src_len, int64_t* dev_lens);
+
+/* ------------------------------------------------------------------------
  * cp_classify -- class of one (Q range, KV range) block pair.
  * [VID] chapter on kernels, overlap and causal masks; [RA] ring topology.
  *

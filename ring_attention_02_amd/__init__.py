@@ -28,7 +28,7 @@ EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
             "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
             "ring_attn_step_jobs", "split_kv_decode_paged", "ring_attn_step_varlen",
-            "cp_gather_rows")
+            "cp_gather_rows", "cp_reorg_index")
 
 
 class RingAttnError(RuntimeError):
@@ -55,6 +55,8 @@ _lib.cp_partition.argtypes = [_vp, _i32, _i32, _i32, _vp, _pi64, _vp, _pi64]
 _lib.cp_slot_mapping.restype = _i32
 _lib.cp_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp]
 _lib.cp_classify.restype = _i32
+_lib.cp_reorg_index.restype = _i32
+_lib.cp_reorg_index.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _pi64, _vp]
 _lib.cp_classify.argtypes = [_i64, _i64, _i64, _i64, _i32, _pi32]
 _lib.ring_attn_step.restype = _i32
 _lib.ring_attn_step.argtypes = [_vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
@@ -148,6 +150,22 @@ def slot_mapping(positions, block_size, interleave, pcp_size, dcp_size, block_ta
                                 dcp_size, _np_ptr(table), 0 if table is None else table.size,
                                 _np_ptr(dev), _np_ptr(slot)), "cp_slot_mapping")
     return dev, slot
+
+
+def reorg_index(seq_lens, block_size, interleave, pcp_size, dcp_size):
+    """Rows of an all-gathered KV buffer in request order: (src_idx int64[sum L],
+    dev_lens int64[W, num_reqs])."""
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+    n = ctypes.c_int64(0)
+    W = pcp_size * dcp_size
+    dev_lens = np.zeros((W, lens.size), dtype=np.int64)
+    _check(_lib.cp_reorg_index(_np_ptr(lens), lens.size, block_size, interleave, pcp_size, dcp_size,
+                               None, ctypes.byref(n), _np_ptr(dev_lens)), "cp_reorg_index")
+    src = np.empty(n.value, dtype=np.int64)
+    if n.value:
+        _check(_lib.cp_reorg_index(_np_ptr(lens), lens.size, block_size, interleave, pcp_size,
+                                   dcp_size, _np_ptr(src), ctypes.byref(n), None), "cp_reorg_index")
+    return src, dev_lens
 
 
 def classify(q_pos0, sq, k_pos0, sk, causal=True):
@@ -450,7 +468,7 @@ def stage_copy(pairs, stream=None):
 
 from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E402
 
-__all__ = ["partition", "slot_mapping", "classify", "ring_attn_step", "ring_attn_step_jobs",
+__all__ = ["partition", "slot_mapping", "reorg_index", "classify", "ring_attn_step", "ring_attn_step_jobs",
            "lse_merge", "stage_copy",
            "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged",
            "ring_attn_step_varlen", "gather_rows", "ZigzagRing", "segmented_prefill",

@@ -9,6 +9,7 @@
 // Splits Long Sequences Across GPUs" (chapter on kernels, overlap and causal
 // masks), with absolute positions so any Q range meets any KV range.
 #include <cstdint>
+#include <algorithm>
 #include <limits>
 #include <vector>
 
@@ -127,6 +128,56 @@ extern "C" int32_t cp_slot_mapping(const int64_t* positions, int64_t n, int32_t 
     device_out[i] = static_cast<int32_t>(lbi % world);
     slot_out[i] = phys * block_size + in_block;
   }
+  return ok();
+}
+
+// vLLM-Ascend "Context Parallel (CP)", MLA chunked prefill with all-gather
+// KV: each device holds, request after request, its slots of the context
+// (placed by the slot mapping); an all-gather concatenates the devices'
+// buffers, so the gathered KV interleaves requests and devices, and
+// reorg_kvcache makes every request's KV contiguous again.  This computes,
+// for every token of every request in original order, its row in the
+// gathered buffer; the device gather (cp_gather_rows) then moves the rows.
+extern "C" int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int32_t block_size,
+                                  int32_t interleave, int32_t pcp_size, int32_t dcp_size,
+                                  int64_t* src_idx, int64_t* src_len, int64_t* dev_lens) {
+  RA_CHECK(num_reqs >= 0, CP_EINVAL, "cp_reorg_index: num_reqs=%d < 0", num_reqs);
+  RA_CHECK(num_reqs == 0 || seq_lens, CP_EINVAL, "cp_reorg_index: NULL seq_lens");
+  RA_CHECK(block_size > 0 && interleave > 0 && pcp_size > 0 && dcp_size > 0, CP_EINVAL,
+           "cp_reorg_index: sizes must be positive (block_size=%d interleave=%d pcp=%d dcp=%d)",
+           block_size, interleave, pcp_size, dcp_size);
+  RA_CHECK(block_size % interleave == 0, CP_EINVAL,
+           "cp_reorg_index: block_size %d is not a multiple of interleave %d", block_size, interleave);
+  int64_t total = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    RA_CHECK(seq_lens[r] >= 0, CP_EINVAL, "cp_reorg_index: seq_lens[%d] < 0", r);
+    total += seq_lens[r];
+  }
+  if (src_len) *src_len = total;
+  const int64_t world = static_cast<int64_t>(pcp_size) * dcp_size;
+  const int64_t vbs = static_cast<int64_t>(block_size) * world;
+  // tokens of request r on device d
+  std::vector<int64_t> len(static_cast<size_t>(world * num_reqs), 0);
+  for (int32_t r = 0; r < num_reqs; ++r)
+    for (int64_t x = 0; x < seq_lens[r]; ++x) ++len[((x % vbs) / interleave % world) * num_reqs + r];
+  if (dev_lens) std::copy(len.begin(), len.end(), dev_lens);
+  if (src_idx == nullptr) return ok();
+  // gathered row of (device d, request r, local slot s) = base[d][r] + s
+  std::vector<int64_t> base(len.size(), 0);
+  int64_t run = 0;
+  for (int64_t d = 0; d < world; ++d)
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      base[d * num_reqs + r] = run;
+      run += len[d * num_reqs + r];
+    }
+  int64_t out = 0;
+  for (int32_t r = 0; r < num_reqs; ++r)
+    for (int64_t x = 0; x < seq_lens[r]; ++x) {
+      const int64_t off = x % vbs, lbi = off / interleave;
+      const int64_t dev = lbi % world;
+      const int64_t slot = (x / vbs) * block_size + (lbi / world) * interleave + off % interleave;
+      src_idx[out++] = base[dev * num_reqs + r] + slot;
+    }
   return ok();
 }
 

@@ -74,20 +74,33 @@ extern "C" int32_t ring_stage_copy(void* const* dsts, const void* const* srcs,
 namespace ringattn {
 namespace {
 
-// One row per group of threads: each thread moves 16-byte units of row i.
+// One wave per row (rows grid-strided over all waves): the row's index is
+// read once, then each lane moves 16-byte units lane, lane + 64, ... with
+// four loads in flight before their stores.
 __global__ void __launch_bounds__(kStageThreads) gather_rows_kernel(u32x4* __restrict__ dst,
                                                                    const u32x4* __restrict__ src,
                                                                    const int64_t* __restrict__ idx,
                                                                    int64_t n, int64_t n_src,
                                                                    int64_t units_per_row) {
-  const int64_t total = n * units_per_row;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStageThreads;
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; u < total; u += stride) {
-    const int64_t row = u / units_per_row, col = u - row * units_per_row;
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kStageThreads / 64);
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (kStageThreads / 64) + (threadIdx.x >> 6); row < n;
+       row += waves) {
     const int64_t from = idx[row];
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (from >= 0 && from < n_src) x = src[from * units_per_row + col];
-    dst[u] = x;
+    const bool valid = from >= 0 && from < n_src;
+    const u32x4* s = src + (valid ? from : 0) * units_per_row;
+    u32x4* d = dst + row * units_per_row;
+    for (int64_t u = lane; u < units_per_row; u += 4 * 64) {
+      u32x4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t v = u + i * 64;
+        x[i] = (valid && v < units_per_row) ? s[v] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (u + i * 64 < units_per_row) d[u + i * 64] = x[i];
+    }
   }
 }
 
@@ -110,8 +123,9 @@ extern "C" int32_t cp_gather_rows(void* dst, const void* src, const int64_t* idx
                s0 >= d0 + static_cast<uintptr_t>(n * row_bytes),
            CP_EINVAL, "cp_gather_rows: dst and src overlap");
   const int64_t units = row_bytes / 16;
-  const int64_t want = (n * units + kStageThreads * 4 - 1) / (kStageThreads * 4);
-  const unsigned blocks = static_cast<unsigned>(want < 4096 ? want : 4096);
+  const int64_t rows_per_block = kStageThreads / 64;
+  const int64_t want = (n + rows_per_block - 1) / rows_per_block;
+  const unsigned blocks = static_cast<unsigned>(want < 8192 ? want : 8192);
   hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kStageThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
                      static_cast<const u32x4*>(src), idx, n, n_src, units);

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 15, declared
+    assert len(declared) == 16, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
@@ -267,3 +267,26 @@ def test_varlen_and_gather_validate_before_launch(ra):
     assert g(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 24), fake, 4, 4, 32, None) == ra.CP_EINVAL
     assert g(fake, ctypes.c_void_p((1 << 20) + 64), fake, 4, 4, 32, None) == ra.CP_EINVAL   # overlap
     assert g(fake, fake, fake, 0, 4, 32, None) == ra.CP_OK
+
+
+@pytest.mark.parametrize("lens,bs,il,pcp,dcp", [([1000, 37, 0, 513], 16, 4, 2, 2), ([4096], 128, 16, 8, 1),
+                                                ([5, 9], 6, 3, 3, 1), ([8, 6], 4, 2, 1, 2), ([], 4, 2, 2, 1)])
+def test_reorg_index_matches_oracle(ra, lens, bs, il, pcp, dcp):
+    import numpy as np
+    from oracle import reorg_index_ref
+    src, dev_lens = ra.reorg_index(lens, bs, il, pcp, dcp)
+    ref_src, ref_lens = reorg_index_ref(lens, bs, il, pcp, dcp)
+    assert np.array_equal(src, ref_src) and np.array_equal(dev_lens, ref_lens)
+
+
+def test_reorg_index_errors(ra):
+    import numpy as np
+    lib = ra.lib()
+    lens = np.array([10, -1], dtype=np.int64)
+    n = ctypes.c_int64(0)
+    assert lib.cp_reorg_index(ctypes.c_void_p(lens.ctypes.data), 2, 4, 2, 2, 1, None, ctypes.byref(n),
+                              None) == ra.CP_EINVAL
+    ok = np.array([10], dtype=np.int64)
+    assert lib.cp_reorg_index(ctypes.c_void_p(ok.ctypes.data), 1, 6, 4, 2, 1, None, ctypes.byref(n),
+                              None) == ra.CP_EINVAL and "multiple" in ra.last_error()
+    assert lib.cp_reorg_index(None, 1, 4, 2, 2, 1, None, ctypes.byref(n), None) == ra.CP_EINVAL

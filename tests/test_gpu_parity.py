@@ -531,3 +531,46 @@ def test_varlen_more_requests_than_one_launch(ra):
     reqs = [(int(rng.integers(0, 90)), int(rng.integers(0, 150)), int(rng.integers(0, 200)),
              int(rng.integers(0, 200))) for _ in range(150)]
     _varlen_case(ra, 64, reqs, 2, 1, 128, 128)
+
+
+def test_allgather_kv_reorg_then_segmented_prefill(ra):
+    """All-gather-KV chunked prefill: each device's KV buffer lists the
+    requests in order (tokens by slot), the all-gather concatenates the
+    devices, the reorganisation gathers every request back into one
+    contiguous, in-order block (bit for bit), and the chunk's queries then
+    attend segment by segment over it."""
+    lens, bs, il, pcp, dcp, hq, hkv, d = [700, 257, 1500], 32, 8, 1, 4, 4, 2, 128
+    W = pcp * dcp
+    ks, vs, k64s, v64s = [], [], [], []
+    for r, L in enumerate(lens):
+        k, k64 = tensor(70 + r, 2, 0, (L, hkv, d), torch.bfloat16)
+        v, v64 = tensor(70 + r, 3, 0, (L, hkv, d), torch.bfloat16)
+        ks.append(k); vs.append(v); k64s.append(k64); v64s.append(v64)
+    dev_k, dev_v = [], []
+    for dv_ in range(W):                     # each device's buffer, built by concatenation
+        pk, pv = [], []
+        for r, L in enumerate(lens):
+            dev, slot = ra.slot_mapping(np.arange(L), bs, il, pcp, dcp)
+            mine = np.nonzero(dev == dv_)[0]
+            order = torch.from_numpy(mine[np.argsort(slot[mine], kind="stable")]).cuda()
+            pk.append(ks[r][order]); pv.append(vs[r][order])
+        dev_k.append(torch.cat(pk)); dev_v.append(torch.cat(pv))
+    gathered_k, gathered_v = torch.cat(dev_k).contiguous(), torch.cat(dev_v).contiguous()   # all-gather
+    src, _ = ra.reorg_index(lens, bs, il, pcp, dcp)
+    src_t = torch.from_numpy(src).cuda()
+    k_r = ra.gather_rows(gathered_k, src_t)
+    v_r = ra.gather_rows(gathered_v, src_t)
+    torch.cuda.synchronize()
+    assert torch.equal(k_r, torch.cat(ks)) and torch.equal(v_r, torch.cat(vs))
+    # the last request's final 200 tokens are the chunk: causal over its whole context
+    r, L, sq = 2, lens[2], 200
+    off = sum(lens[:r])
+    q, q64 = tensor(79, 1, 0, (1, sq, hq, d), torch.bfloat16)
+    o = torch.empty((1, sq, hq, d), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    ra.segmented_prefill(q, k_r[None, off:off + L], v_r[None, off:off + L], o, lse, q_pos0=L - sq,
+                         segment=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_ref(q64, k64s[r][None], v64s[r][None], L - sq + np.arange(sq), np.arange(L),
+                                  True)
+    compare(host64(o), host64(lse), ro, rl, BF16_O, BF16_LSE, "reorganised chunk")

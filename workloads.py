@@ -193,3 +193,20 @@ def varlen_setup(n_req=16, hq=32, hkv=8, d=128, seed_cfg=6):
     zeros = np.zeros(n_req, dtype=np.int64)
     return dict(q=q, k=k, v=v, o=o, lse=lse, cu=cu, pos=zeros, lens=lens, hq=hq, hkv=hkv, d=d,
                 pairs=pairs, flops=pairs * hq * 4 * d)
+
+
+def reorg_setup():
+    """All-gather-KV reorganisation at the chunked-prefill (MLA) scale: the
+    135,168-token context split into 4 requests, placed on 8 devices
+    (block 128, interleave 16), all-gathered: K [N, 128, 192] and
+    V [N, 128, 128] bf16 in gathered order, and the request-order row index."""
+    import ring_attention_02_amd as ra
+    torch = _torch()
+    c = CONFIGS[5]
+    lens = [50000, 40000, 30000, c["kv_len"] - 120000]
+    n = sum(lens)
+    gk = si.device_normal(5, K_ID, 7, (n, c["heads"], c["d_qk"]), torch.bfloat16, "cuda")
+    gv = si.device_normal(5, V_ID, 7, (n, c["heads"], c["d_v"]), torch.bfloat16, "cuda")
+    src, _ = ra.reorg_index(lens, 128, 16, 1, 8)
+    return dict(gk=gk, gv=gv, idx=torch.from_numpy(src).cuda(), lens=lens, n=n,
+                bytes=2 * (gk.numel() + gv.numel()) * 2 + src.size * 8)
