@@ -11,18 +11,27 @@
 // meet any K/V block of a zigzag partition.
 //
 // gfx950 design (bf16 path):
-//  * workgroup = 4 waves = 128 query rows of one (batch, query head); each
-//    wave owns 32 rows whose Q fragment stays in registers for the sweep;
-//  * K/V tiles of 64 keys go global -> registers (prefetched one tile ahead)
-//    -> LDS; K rows padded by 16 B, V rows by 64 B (bank-conflict-free
-//    b128 / transposed reads);
+//  * one launch is one ring step: up to 4 query chunks ("jobs"), each over up
+//    to 4 K/V segments at their own positions, or up to 64 packed requests
+//    (varlen); it can also copy the ring's next K/V block into the idle
+//    staging slot (forwarded ranges);
+//  * workgroup = 4 waves = 128 query rows of one (job, batch, query head);
+//    each wave owns 32 rows whose Q fragment stays in registers for the
+//    sweep; grids under two workgroups per CU use 8 waves (two key-split
+//    halves merged through LDS), and a complementary two-job step can pair
+//    two query tiles in one workgroup;
+//  * K/V tiles of 64 keys go HBM -> LDS with bounded buffer loads (one
+//    descriptor per segment, the tile offset in soffset; rows past a segment
+//    read as zero), two stages each, XOR-swizzled 16-byte chunks for
+//    conflict-free b128 and transposed reads, one barrier per tile;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand,
 //    Q^T as B), so each lane holds 32 scores of ONE query row: the row max
 //    and row sum are in-register plus one cross-half exchange;
 //  * P^T stays in registers and is the B operand of O^T += V^T P^T; the
 //    contraction order over keys is permuted to match the score layout, and
 //    V^T is read with ds_read_b64_tr_b16 from row-major V in LDS;
-//  * exp2-domain online softmax; fully visible tiles skip the mask.
+//  * exp2-domain online softmax with a lazily raised running max; tiles that
+//    need no mask skip it with one compare.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -1,10 +1,13 @@
 // Host-side index logic of context parallelism: the head-tail (zigzag)
 // partition with its restore index, the interleaved virtual-block slot
-// mapping, and the full / diagonal / skip classification of block pairs.
+// mapping, the row index that reorganises an all-gathered KV cache by
+// request, and the full / diagonal / skip classification of block pairs.
 //
 // Partition: vLLM-Ascend developer guide "Context Parallel (CP)", section
 // "Prefill context parallel (PCP)", head-tail token partition paragraph.
 // Slot mapping: same guide, section "How it works / Block table".
+// Reorganisation: same guide, PCP chunked-prefill paragraph and the MLA
+// prefill note on all-gather KV.
 // Classification: causal masking per block, video "How Context Parallelism
 // Splits Long Sequences Across GPUs" (chapter on kernels, overlap and causal
 // masks), with absolute positions so any Q range meets any KV range.

@@ -7,6 +7,11 @@
 // transfer.  On one GPU the transfer is a device-to-device copy of the
 // block's pieces into the idle slot; this kernel moves all of them in one
 // launch (16-byte vector loads and stores, grid-stride over the total).
+//
+// Also here: the row gather that applies an index on the device -- the
+// restore index of the head-tail partition (vLLM-Ascend "Context Parallel
+// (CP)", PCP head-tail paragraph) and the reorganisation of an all-gathered
+// KV cache by request (same guide, MLA prefill note).
 #include <hip/hip_runtime.h>
 
 #include "kernels_common.h"
