@@ -624,8 +624,6 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   if (my_n > 0) dma_k(tile(0), 0);
   if (my_n > 1) dma_k(tile(1), 1);
   if (my_n > 0) dma_v(tile(0), 0);
-  // Stores of this workgroup's slice of the forwarded block (its loads were
-  // issued first); they drain under the prologue's wait.
 
   if (n_iter > 0) {
     f32x16 s_cur[2], s_nxt[2];
