@@ -251,8 +251,10 @@ struct FwdSlice {
 // tiles of the same 128 query rows while waves 0-3 sweep the even ones, and
 // the two softmax states are merged through LDS at the end.  This keeps two
 // waves per SIMD even when a launch has only one workgroup per CU.
-template <int DQK, int DV, int SPLIT, bool PAIRED, bool VARLEN>
-__global__ void __launch_bounds__(kThreads * SPLIT, 2)
+// ROWS = 2 (large grids): 8 waves own 256 query rows and share every K/V
+// tile, halving the tile loads and LDS writes per FLOP.
+template <int DQK, int DV, int SPLIT, bool PAIRED, bool VARLEN, int ROWS = 1>
+__global__ void __launch_bounds__(kThreads * SPLIT * ROWS, 2)
 attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   const JobArgs& a = base_args(args);
@@ -265,12 +267,15 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave = wave_all & 3;                  // wave within its half: owns 32 query rows
+  static_assert(ROWS == 1 || SPLIT == 1, "256-row tiles use one key sweep");
+  constexpr int BM = kBM * ROWS;                  // query rows per workgroup
+  constexpr int LW = 4 * ROWS;                    // waves that load (and read) each tile
+  const int wave = ROWS == 2 ? wave_all : (wave_all & 3);  // owns 32 query rows
   const int half = SPLIT == 1 ? 0 : wave_all >> 2;  // which alternate key tiles it sweeps
   uint16_t* const Kh = Ks + half * 2 * C::KTILE;
   uint16_t* const Vh = Vs + half * 2 * C::VTILE;
   // Loads of this workgroup's first slice of the forwarded block go out first.
-  FwdSlice<kThreads * SPLIT> fwd;
+  FwdSlice<kThreads * SPLIT * ROWS> fwd;
   if (a.n_fwd > 0) fwd.load_first(a, blockIdx.x, tid);
 
   const int col = lane & 31;  // query row within the wave (B / C column)
@@ -352,14 +357,14 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     else return job.seg[sg].k_pos0;
   };
   const int64_t sq = j_sq();
-  if (VARLEN && static_cast<int64_t>(qt) * kBM >= sq) continue;   // past this request's queries
+  if (VARLEN && static_cast<int64_t>(qt) * BM >= sq) continue;   // past this request's queries
   const uint16_t* jq = static_cast<const uint16_t*>(job.q);
   if constexpr (VARLEN) jq += static_cast<int64_t>(args.req[jb].q_start) * a.hq * DQK;
 
   const uint16_t* __restrict__ qg = jq;
 
-  const int64_t q_first = static_cast<int64_t>(qt) * kBM;
-  const int64_t q_last = min(sq, q_first + kBM) - 1;  // last valid local row of the WG
+  const int64_t q_first = static_cast<int64_t>(qt) * BM;
+  const int64_t q_last = min(sq, q_first + BM) - 1;  // last valid local row of the WG
   const int64_t wq0 = q_first + wave * 32;              // first row of this wave
   const int64_t my_row = wq0 + col;
   const bool row_valid = my_row < sq;
@@ -422,16 +427,18 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // to its slot, at a loop-invariant byte offset inside the tile.
   const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
   const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
-  uint32_t koffb[C::KDMA], voffb[C::VDMA];
+  constexpr int KDMA_W = C::KDMA / ROWS, VDMA_W = C::VDMA / ROWS;   // per wave
+  static_assert(KDMA_W * ROWS == C::KDMA && VDMA_W * ROWS == C::VDMA, "tile loads split evenly");
+  uint32_t koffb[KDMA_W], voffb[VDMA_W];
 #pragma unroll
-  for (int i = 0; i < C::KDMA; ++i) {
-    const int p = (i * 4 + wave) * 64 + lane;
+  for (int i = 0; i < KDMA_W; ++i) {
+    const int p = (i * LW + wave) * 64 + lane;
     const int row = p / C::KCPR;
     koffb[i] = static_cast<uint32_t>((row * row_elems_k + kswz<C::KCPR>(p % C::KCPR, row) * 8) * 2);
   }
 #pragma unroll
-  for (int i = 0; i < C::VDMA; ++i) {
-    const int p = (i * 4 + wave) * 64 + lane;
+  for (int i = 0; i < VDMA_W; ++i) {
+    const int p = (i * LW + wave) * 64 + lane;
     const int row = p / C::VCPR;
     voffb[i] = static_cast<uint32_t>((row * row_elems_v + vswz<C::VCPR>(p % C::VCPR, row) * 8) * 2);
   }
@@ -463,9 +470,9 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     const int soff = (vt - kcur.base_vt) * tile_bytes_k;
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
-    for (int i = 0; i < C::KDMA; ++i)
+    for (int i = 0; i < KDMA_W; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          kcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
           static_cast<int>(koffb[i]), soff, 0, 0);
   };
   auto dma_v = [&](int vt, int stage) {
@@ -473,9 +480,9 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     const int soff = (vt - vcur.base_vt) * tile_bytes_v;
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
-    for (int i = 0; i < C::VDMA; ++i)
+    for (int i = 0; i < VDMA_W; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 64 * 8), 16,
+          vcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
           static_cast<int>(voffb[i]), soff, 0, 0);
   };
 
@@ -893,7 +900,18 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
     }
   }
   RA_CHECK(!args.paired, CP_EUNSUPPORTED, "ring_attn_step: paired launch needs the 8-wave variant");
-  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
+  // Large grids: 256-row workgroups while that still leaves two per CU.
+  const int64_t n_wide = (args.sq + 2 * kBM - 1) / (2 * kBM);
+  const int64_t total_wide = n_wide * args.n_jobs * args.hq * batch;
+  if (total_wide >= 2 * static_cast<int64_t>(device_cus())) {
+    args.n_qtiles = static_cast<int32_t>(n_wide);
+    args.total_wgs = static_cast<int32_t>(total_wide);
+    if (args.n_fwd > 0) args.fwd_per_wg = (args.fwd_end[kMaxFwd - 1] + total_wide - 1) / total_wide;
+    hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2>), dim3(static_cast<unsigned>(total_wide)),
+                       dim3(2 * kThreads), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
+  }
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
   return CP_OK;
@@ -920,6 +938,8 @@ int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
       return CP_OK;
     }
   }
+  // (128-row tiles here: packed requests end on ragged rows, which 256-row
+  // tiles waste -- measured slower for the varlen mix.)
   hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, true>), grid, dim3(kThreads), 0, stream, args);
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));

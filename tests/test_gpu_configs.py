@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import host64, compare, say, F32_O, BF16_O, BF16_LSE
+from gpu_util import host64, compare, say, tensor, F32_O, BF16_O, BF16_LSE
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -171,4 +171,32 @@ def test_c5_segmented_sampled(ra):
     _sampled_rows_check(o, lse, q_rows, lambda g: host64(k[0, :, g]), lambda g: host64(v[0, :, g]),
                         q_pos, hh, 1, "C5")
     del w, k, v
+    _release()
+
+
+@pytest.mark.parametrize("dqk,dv,hq,hkv", [(128, 128, 4, 2), (64, 64, 4, 4), (192, 128, 4, 1)])
+def test_large_grid_ragged_sampled(ra, dqk, dv, hq, hkv):
+    """A grid large enough for the 256-row workgroups (130 full row tiles and
+    a ragged 37-row tail, 4 heads), causal with a position offset between Q
+    and K; sampled rows against the oracle (tile edges, the tail, random)."""
+    sq, sk, q0 = 256 * 130 + 37, 256 * 130 + 37 + 500, 500
+    q, _ = tensor(81, 1, 0, (1, sq, hq, dqk), torch.bfloat16)
+    k, _ = tensor(81, 2, 0, (1, sk, hkv, dqk), torch.bfloat16)
+    v, _ = tensor(81, 3, 0, (1, sk, hkv, dv), torch.bfloat16)
+    o = torch.empty((1, sq, hq, dv), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    ra.ring_attn_step(q, k, v, o, lse, q_pos0=q0, k_pos0=0, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(81)
+    toks = sorted({0, 1, 31, 32, 127, 128, 255, 256, 511, sq - 38, sq - 37, sq - 1}
+                  | set(rng.integers(0, sq, 20).tolist()))
+    rows = [(t, hd) for t in toks for hd in range(hq)]
+    tt = np.array([r[0] for r in rows])
+    hh = np.array([r[1] for r in rows])
+    ti, hi = torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()
+    say(f"large grid d {dqk}/{dv}: {len(rows)} sampled rows")
+    _sampled_rows_check(host64(o[0][ti, hi]), host64(lse[0][ti, hi]), host64(q[0][ti, hi]),
+                        lambda g: host64(k[0, :, g]), lambda g: host64(v[0, :, g]), q0 + tt, hh,
+                        hq // hkv, "large grid")
+    del q, k, v, o, lse
     _release()
