@@ -1,0 +1,36 @@
+"""bench.py's command-line contract that can be checked without a GPU."""
+
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""          # no JSON line for a refused run
+
+
+def test_profiled_traffic_matches_the_committed_summary():
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.profiled_traffic("attn_step_bf16_zigzag_seq8192_cp4.md", "attn_step.hip")
+    # null is allowed only when the kernel source changed after the counters were taken
+    text = open(os.path.join(ROOT, "profiles", "attn_step_bf16_zigzag_seq8192_cp4.md")).read()
+    assert "traffic_bytes_per_launch:" in text
+    if t is not None:
+        assert 1e8 < t < 2e8
+
+
+def test_roofline_entry_shape():
+    sys.path.insert(0, ROOT)
+    import bench
+    e = bench.roofline_entry("mfma", 500.0, 2500.0, "TFLOP/s", 123)
+    assert e == {"bound": "mfma", "achieved": 500.0, "peak": 2500.0, "unit": "TFLOP/s",
+                 "frac": 0.2, "traffic": 123}
+    json.dumps(e)
