@@ -587,11 +587,18 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   const int my_n = ntiles > half ? (ntiles - half + SPLIT - 1) / SPLIT : 0;
   const int n_iter = (ntiles + SPLIT - 1) / SPLIT;
   auto tile = [&](int j) { return j * SPLIT + half; };
-  // Online softmax of tile j (exp2 domain) plus, when there is a next tile,
-  // its scores on MFMA interleaved with the exponentials.  Both halves of a
+  // Online softmax of tile j (exp2 domain) plus the scores of tile j+1 on
+  // MFMA interleaved with the exponentials.  The next scores are computed
+  // even after the last tile (from a stale stage, then dropped): with no
+  // branch around them the exponentials and the MFMAs share one basic block
+  // and the interleave holds.  Both halves of a
   // row share m_run.  It is raised only when some row of the wave gained more
   // than tau (log2 units); otherwise the stale max stays, which is exact
   // because numerator and denominator share it, and P stays below 2^tau.
+  // Fast form (d_qk <= 128, unpaired): next scores always computed and the
+  // loop unrolled by two so the score buffers swap without copies.  The
+  // other kernels keep a branch and a copy: there the unrolled body spills.
+  constexpr bool kAlwaysNext = DQK <= 128 && !PAIRED;
   auto softmax_and_next_scores = [&](int j, f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, int next_stage) {
     mask_tile(tile(j), s_cur);
     float mx = kNegInf;
@@ -612,7 +619,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
       m_run = m_new;
     }
     const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
-    if (j + 1 < my_n) {
+    if (kAlwaysNext || j + 1 < my_n) {
       qk(next_stage, s_nxt);               // MFMA: scores of tile j+1 ...
       l_run += exps(s_cur, pb, neg_mc);    // ... interleaved with the VALU exponentials of tile j
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -642,19 +649,39 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (my_n > 0) qk(0, s_cur);
-    for (int j = 0; j < n_iter; ++j) {
+    // One iteration; P = j & 1 is the parity of j, so the stage offsets are
+    // constants and the two score buffers swap roles without copies.
+    auto iteration = [&](int j, auto parity, f32x16* sc, f32x16* sn) {
+      constexpr int P = decltype(parity)::value;
       // The loads issued at the start of iteration j-1 have landed for every
       // wave, and every wave is done with iteration j-1.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);        // K stage j%2 held K_j (read in j-1)
-      if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);  // V stage (j+1)%2 held V_{j-1}
+      if (j + 2 < my_n) dma_k(tile(j + 2), P);        // K stage j%2 held K_j (read in j-1)
+      if (j + 1 < my_n) dma_v(tile(j + 1), P ^ 1);    // V stage (j+1)%2 held V_{j-1}
       if (j < my_n) {
-        softmax_and_next_scores(j, s_cur, s_nxt, pb, (j + 1) & 1);
-        pv(j & 1, pb);                                     // MFMA: O += P_j V_j
+        softmax_and_next_scores(j, sc, sn, pb, P ^ 1);
+        pv(P, pb);                                     // MFMA: O += P_j V_j
       }
+    };
+    if constexpr (kAlwaysNext) {
+      for (int j = 0; j < n_iter; j += 2) {
+        iteration(j, std::integral_constant<int, 0>{}, s_cur, s_nxt);
+        if (j + 1 < n_iter) iteration(j + 1, std::integral_constant<int, 1>{}, s_nxt, s_cur);
+      }
+    } else {
+      for (int j = 0; j < n_iter; ++j) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);
+        if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);
+        if (j < my_n) {
+          softmax_and_next_scores(j, s_cur, s_nxt, pb, (j + 1) & 1);
+          pv(j & 1, pb);
+        }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+      }
     }
   }
 
