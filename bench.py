@@ -11,7 +11,9 @@ computes the (Q chunk, K/V chunk) pairs of the current block (7 FULL, 2 DIAG
 and 7 SKIP pairs overall, merged in place) and copies the next K/V block
 into the idle staging slot.
 `value` is algorithmic causal-attention TFLOP/s: visible (q, k) pairs x
-heads x (2 d_qk + 2 d_v) per sweep / time per sweep.
+heads x (2 d_qk + 2 d_v) per sweep / time per sweep.  The same sweep with
+the staging copies on a side stream (ring_stage_copy launches ordered by
+events) is timed beside it and reported under "launch".
 
 Also reported in the same line (unless --primary-only): the long zigzag
 prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
@@ -180,9 +182,15 @@ def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
     ring, q, o, lse = w["ring"], w["q_local"], w["o"], w["lse"]
     eager = time_steps(lambda: ring.run(q, o, lse), steps, warmup)
     sec = eager
+    side_sec = None
     if use_graph:
         graph = ring.capture(q, o, lse)
         sec = time_steps(graph.replay, steps, warmup)
+        if cfg_id == 2:
+            # the same sweep with the staging copies on a side stream
+            side_graph = ring.capture(q, o, lse, side_copies=True)
+            side_sec = time_steps(side_graph.replay, steps, warmup)
+            del side_graph
     launches = zigzag_launches(w)
     reps = max(2, min(steps, 20)) if cfg_id == 2 else 1
     mean_ms = kernel_launch_stats(launches, reps)
@@ -192,7 +200,8 @@ def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
     diag_ms = kernel_launch_stats(zigzag_launches(w, ra.DIAG), reps)
     return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=len(launches),
                         flops_per_launch=flops_per_launch, achieved_tflops=achieved,
-                        full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3)
+                        full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3,
+                        side_ms=None if side_sec is None else side_sec * 1e3)
 
 
 def decode_bench(steps, warmup, paged=False):
@@ -365,7 +374,8 @@ def main():
                    "timing": "HIP-graph replay of the step's kernels back to back, HIP events"},
         "launch": {"mode": "HIP graph replay of the whole sweep (one launch per ring "
                            "step, next block's copy inside it)",
-                   "eager_ms_per_step": round(l2["eager_ms"], 4)},
+                   "eager_ms_per_step": round(l2["eager_ms"], 4),
+                   "side_stream_copies_ms_per_step": round(l2["side_ms"], 4)},
     }
     del w2["ring"]
     if not args.no_cpu_baseline:

@@ -13,10 +13,12 @@ a block is a copy into one of two staging slots, made one step ahead so it
 overlaps the attention of the current block: the double buffering of the
 video "How Context Parallelism Splits Long Sequences Across GPUs" (chapter
 on the wire budget) and of the Excalidraw "Context Parallel (CP) / Ring
-Attention" diagram (rotation overlapped with local attention).  The copy
-rides in the ring step's own launch (its forwarded ranges), so a sweep is
-one stream of one launch per step.  Step 0 uses the rank's own block in
-place.
+Attention" diagram (rotation overlapped with local attention).  By default
+the copy rides in the ring step's own launch (its forwarded ranges), so a
+sweep is one stream of one launch per step.  With a copy stream the copies
+run there instead, ordered by events: block t+1 lands before step t+1 and
+is written only after the step that last read its slot.  Step 0 uses the
+rank's own block in place.
 """
 
 import math
@@ -75,22 +77,46 @@ class ZigzagRing:
                     out.append((t, qi, kj, classify(qp * c, c, kp * c, c, True)))
         return out
 
-    def run(self, q_local, o, lse, scale=None, on_launch=None):
+    def run(self, q_local, o, lse, scale=None, on_launch=None, copy_stream=None):
         """Sweep every ring step; o [1, 2c, hq, dv] / lse [1, 2c, hq] end final.
 
         Step t's launch computes with the block of step t and carries the
-        copy of the block of step t + 1 into the other slot.
+        copy of the block of step t + 1 into the other slot.  With
+        copy_stream (a torch stream) the copies run on it instead, in
+        ring_stage_copy launches ordered against the steps by events.
         on_launch(step, q_index, kv_index, cls, fn) may wrap each launch (the
         bench uses it to time launches); fn() performs the launch.
         """
         c = self.chunk
         first = [True, True]
+        side = copy_stream is not None
+        if side:
+            torch = _torch()
+            main = torch.cuda.current_stream()
+            copied = {}                              # block t -> event after its copy
+            read_done = {}                           # step t -> event after its launch
+            copy_stream.wait_stream(main)
+
+            def issue_copy(u):
+                # block u goes to slot u % 2, last read by step u - 2
+                with torch.cuda.stream(copy_stream):
+                    if u - 2 >= 1:
+                        copy_stream.wait_event(read_done[u - 2])
+                    stage_copy(self.forward_pairs(u))
+                    copied[u] = torch.cuda.Event()
+                    copied[u].record(copy_stream)
+
+            for u in (1, 2):
+                if u < self.cp:
+                    issue_copy(u)
         for t, kv_parts in enumerate(self.steps):
             if t == 0:
                 ks, vs = self.local_slices(0)
             else:
                 ks, vs = self.kbuf[t % 2], self.vbuf[t % 2]
-            fwd = self.forward_pairs(t + 1) if t + 1 < self.cp else []
+                if side:
+                    main.wait_event(copied[t])
+            fwd = self.forward_pairs(t + 1) if t + 1 < self.cp and not side else []
             # One launch per ring step: each local Q part is a job over the
             # block's parts it can see (SKIP parts are left out).
             jobs, step_cls = [], FULL
@@ -116,23 +142,32 @@ class ZigzagRing:
                     on_launch(t, 0, 0, step_cls, fn)
             elif fwd:
                 stage_copy(fwd)
+            if side:
+                read_done[t] = torch.cuda.Event()
+                read_done[t].record(main)
+                if t >= 1 and t + 2 < self.cp:
+                    issue_copy(t + 2)
+        if side:
+            main.wait_stream(copy_stream)
         return o, lse
 
-    def capture(self, q_local, o, lse, scale=None):
+    def capture(self, q_local, o, lse, scale=None, side_copies=False):
         """Record one whole sweep as a HIP graph.
 
         Replaying the graph runs the same launches as run() without the
         host-side cost of issuing them one by one; the buffers passed here
-        are the ones every replay reads and writes.
+        are the ones every replay reads and writes.  side_copies records the
+        copy-stream form (two streams joined in the graph).
         """
         torch = _torch()
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         stream = torch.cuda.Stream()                      # default priority
+        side = torch.cuda.Stream() if side_copies else None
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             with torch.cuda.graph(graph, stream=stream):
-                self.run(q_local, o, lse, scale=scale)
+                self.run(q_local, o, lse, scale=scale, copy_stream=side)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
         return graph

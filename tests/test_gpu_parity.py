@@ -258,6 +258,43 @@ def test_zigzag_graph_replay_matches_eager(ra):
         assert torch.equal(o, o_eager)
 
 
+def test_zigzag_copy_stream_matches_in_launch_copies(ra):
+    """Staging copies on a side stream (eager, and captured as a two-stream
+    graph replayed several times) give the same sweep bit for bit as the
+    copies carried in the step launches; cp 4 exercises the slot reuse
+    (block 3 waits for step 1 to finish reading slot 1)."""
+    seq, cp, rank, h, d = 4096, 4, 0, 4, 128
+    say(f"zigzag copy stream: seq {seq} cp {cp} rank {rank}")
+    k, _ = tensor(23, 2, 0, (1, seq, h, d), torch.bfloat16)
+    v, _ = tensor(23, 3, 0, (1, seq, h, d), torch.bfloat16)
+    q_all, _ = tensor(23, 1, 0, (1, seq, h, d), torch.bfloat16)
+    local, _ = ra.partition([seq], cp, rank)
+    q_local = q_all.index_select(1, torch.from_numpy(local).cuda()).contiguous()
+    ring = ra.ZigzagRing(k, v, cp, rank)
+    o = torch.empty((1, len(local), h, d), device="cuda")
+    lse = torch.empty((1, len(local), h), device="cuda")
+    ring.run(q_local, o, lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    o.zero_()
+    ring.run(q_local, o, lse, copy_stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), "eager copy stream"
+    graph = ring.capture(q_local, o, lse, side_copies=True)
+    for i in range(3):
+        o.fill_(float(i + 1))
+        lse.fill_(-float(i + 1))
+        for buf in ring.kbuf + ring.vbuf:           # stale slots must be rewritten
+            buf.fill_(float(i))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), f"replay {i}"
+        ring.run(q_local, o, lse)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_peaked_scores_exercise_max_raises(ra, causal):
     """Large score range (queries scaled x8, some keys planted equal to a
