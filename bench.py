@@ -49,6 +49,8 @@ def parse():
                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     p.add_argument("--sweep-only", type=int, default=0, metavar="K",
                    help="only replay the zigzag sweep graph K times (for counter passes)")
+    p.add_argument("--decode-only", type=int, default=0, metavar="K",
+                   help="only run the sharded decode kernel K times (for counter passes)")
     return p.parse_args()
 
 
@@ -64,6 +66,27 @@ def sweep_only(reps):
     torch.cuda.synchronize()
     print(json.dumps({"sweep_replays": reps, "launches_per_sweep": len(zigzag_launches(w))}),
           flush=True)
+
+
+def decode_only(reps):
+    """The sharded GQA decode kernel alone, K launches (no merge), so
+    per-dispatch counters and durations cover exactly that kernel."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.decode_setup()
+    o_parts = torch.empty((w["n_shards"], w["B"], w["hq"], w["d"]), device="cuda")
+    lse_parts = torch.empty((w["n_shards"], w["B"], w["hq"]), device="cuda")
+    for _ in range(reps):
+        ra.split_kv_decode(w["q"], w["ks"], w["vs"], shard_lens=w["lens"], o_parts=o_parts,
+                           lse_parts=lse_parts)
+    torch.cuda.synchronize()
+    print(json.dumps({"decode_launches": reps, "kernel_bytes": decode_kernel_bytes(w)}), flush=True)
+
+
+def decode_kernel_bytes(w):
+    """Algorithmic bytes of one decode launch: K and V once, Q, partials written."""
+    return w["kv_bytes"] + w["q"].numel() * 2 + w["n_shards"] * w["B"] * w["hq"] * (w["d"] + 1) * 4
 
 
 def calibrate_copy():
@@ -149,10 +172,10 @@ def profiled_traffic(summary, source):
     except OSError:
         return None
     sha = hashlib.sha256(src).hexdigest()[:16]
+    key = f"kernel source sha256 prefix ({source})"
     fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and
-                  line.split(": ", 1)[0] in ("kernel source sha256 prefix (attn_step.hip)",
-                                              "traffic_bytes_per_launch"))
-    if fields.get("kernel source sha256 prefix (attn_step.hip)", "").strip() != sha:
+                  line.split(": ", 1)[0] in (key, "traffic_bytes_per_launch"))
+    if fields.get(key, "").strip() != sha:
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
 
@@ -237,7 +260,7 @@ def decode_bench(steps, warmup, paged=False):
         torch.cuda.synchronize()
         durs.append(s.elapsed_time(e))
     kern_ms = float(np.mean(durs))
-    kern_bytes = w["kv_bytes"] + w["q"].numel() * 2 + w["n_shards"] * w["B"] * w["hq"] * (w["d"] + 1) * 4
+    kern_bytes = decode_kernel_bytes(w)
     return w, sec, dict(kernel_ms=kern_ms, kernel_bytes=kern_bytes,
                         kernel_gbs=kern_bytes / (kern_ms * 1e-3) / 1e9)
 
@@ -350,6 +373,9 @@ def main():
     if args.sweep_only:
         sweep_only(args.sweep_only)
         return
+    if args.decode_only:
+        decode_only(args.decode_only)
+        return
 
     log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
     w2, sec2, l2 = zigzag_bench(2, args.steps, args.warmup)
@@ -403,7 +429,8 @@ def main():
             sec["decode_gqa_8_shards"] = {
                 "value": round(w3["bytes"] / s3 / 1e9, 1), "unit": "GB/s",
                 "ms_per_step": round(s3 * 1e3, 4), "bytes_per_step": w3["bytes"],
-                "roofline": roofline_entry("hbm", l3["kernel_gbs"], PEAK_HBM_GBS, "GB/s"),
+                "roofline": roofline_entry("hbm", l3["kernel_gbs"], PEAK_HBM_GBS, "GB/s",
+                                           profiled_traffic("decode_bf16_gqa_8shards.md", "decode.hip")),
                 "kernel_ms": round(l3["kernel_ms"], 4)}
             del w3
             torch.cuda.empty_cache()

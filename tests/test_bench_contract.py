@@ -27,6 +27,25 @@ def test_profiled_traffic_matches_the_committed_summary():
         assert 1e8 < t < 2e8
 
 
+def test_decode_traffic_matches_the_committed_summary():
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.profiled_traffic("decode_bf16_gqa_8shards.md", "decode.hip")
+    text = open(os.path.join(ROOT, "profiles", "decode_bf16_gqa_8shards.md")).read()
+    assert "traffic_bytes_per_launch:" in text
+    if t is not None:
+        # K + V of 8 shards x 64 requests x 16384 tokens x 8 kv heads x 128 x bf16, read once
+        kv = 2 * 8 * 64 * 16384 * 8 * 128 * 2
+        assert kv <= t < 1.01 * kv
+
+
+def test_summary_for_another_source_is_not_used():
+    sys.path.insert(0, ROOT)
+    import bench
+    # the ring-step summary carries no hash of decode.hip
+    assert bench.profiled_traffic("attn_step_bf16_zigzag_seq8192_cp4.md", "decode.hip") is None
+
+
 def test_roofline_entry_shape():
     sys.path.insert(0, ROOT)
     import bench
