@@ -51,6 +51,8 @@ def parse():
                    help="only replay the zigzag sweep graph K times (for counter passes)")
     p.add_argument("--decode-only", type=int, default=0, metavar="K",
                    help="only run the sharded decode kernel K times (for counter passes)")
+    p.add_argument("--merge-only", type=int, default=0, metavar="K",
+                   help="only run the standalone LSE merge K times (for counter passes)")
     return p.parse_args()
 
 
@@ -317,17 +319,33 @@ def reorg_bench(steps, warmup):
     return w, sec
 
 
-def merge_bench(steps, warmup):
+def merge_setup():
     import torch
-    import ring_attention_02_amd as ra
     rows, dv, n = 131072 * 64, 128, 2       # the long prefill's rows, two partials
     o_parts = torch.randn((n, rows, dv), device="cuda")
     lse_parts = torch.randn((n, rows), device="cuda")
     o = torch.empty((rows, dv), device="cuda")
     lse = torch.empty((rows,), device="cuda")
+    nbytes = (n * rows * (dv + 1) + rows * (dv + 1)) * 4   # parts read, result written
+    return o_parts, lse_parts, o, lse, nbytes
+
+
+def merge_bench(steps, warmup):
+    import ring_attention_02_amd as ra
+    o_parts, lse_parts, o, lse, nbytes = merge_setup()
     sec = time_steps(lambda: ra.lse_merge(o_parts, lse_parts, o_out=o, lse_out=lse), steps, warmup)
-    nbytes = (n * rows * (dv + 1) + rows * (dv + 1)) * 4
     return sec, nbytes
+
+
+def merge_only(reps):
+    """The standalone LSE merge alone, K launches, for counter passes."""
+    import torch
+    import ring_attention_02_amd as ra
+    o_parts, lse_parts, o, lse, nbytes = merge_setup()
+    for _ in range(reps):
+        ra.lse_merge(o_parts, lse_parts, o_out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    print(json.dumps({"merge_launches": reps, "bytes_per_launch": nbytes}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -375,6 +393,9 @@ def main():
         return
     if args.decode_only:
         decode_only(args.decode_only)
+        return
+    if args.merge_only:
+        merge_only(args.merge_only)
         return
 
     log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
@@ -479,7 +500,8 @@ def main():
             s6, b6 = merge_bench(max(5, args.steps), 2)
             sec["lse_merge_2x8M"] = {
                 "value": round(b6 / s6 / 1e9, 1), "unit": "GB/s", "ms_per_step": round(s6 * 1e3, 4),
-                "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s")}
+                "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s",
+                                           profiled_traffic("lse_merge_2x8M.md", "lse_merge.hip"))}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
 

@@ -39,6 +39,16 @@ def test_decode_traffic_matches_the_committed_summary():
         assert kv <= t < 1.01 * kv
 
 
+def test_merge_traffic_matches_the_committed_summary():
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.profiled_traffic("lse_merge_2x8M.md", "lse_merge.hip")
+    if t is not None:
+        rows = 131072 * 64
+        algorithmic = 3 * rows * 129 * 4          # two partials read, one result written
+        assert algorithmic <= t < 1.01 * algorithmic
+
+
 def test_summary_for_another_source_is_not_used():
     sys.path.insert(0, ROOT)
     import bench
