@@ -151,13 +151,16 @@ class ZigzagRing:
             main.wait_stream(copy_stream)
         return o, lse
 
-    def capture(self, q_local, o, lse, scale=None, side_copies=False):
-        """Record one whole sweep as a HIP graph.
+    def capture(self, q_local, o, lse, scale=None, side_copies=False, sweeps=1):
+        """Record whole sweeps as a HIP graph.
 
         Replaying the graph runs the same launches as run() without the
         host-side cost of issuing them one by one; the buffers passed here
         are the ones every replay reads and writes.  side_copies records the
-        copy-stream form (two streams joined in the graph).
+        copy-stream form (two streams joined in the graph); sweeps > 1
+        records that many complete sweeps back to back (each one recomputes
+        o / lse from the same inputs), so a replay pays one graph launch for
+        all of them.
         """
         torch = _torch()
         torch.cuda.synchronize()
@@ -167,7 +170,8 @@ class ZigzagRing:
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             with torch.cuda.graph(graph, stream=stream):
-                self.run(q_local, o, lse, scale=scale, copy_stream=side)
+                for _ in range(sweeps):
+                    self.run(q_local, o, lse, scale=scale, copy_stream=side)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
         return graph

@@ -95,6 +95,35 @@ def test_skip_pair_writes_identity_or_nothing(ra):
     assert torch.all(o == 0.0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_key_and_query_blocks(ra, dtype):
+    """sk = 0: a non-accumulating step writes O = 0 and LSE = -inf (the oracle
+    over no keys), an accumulating one leaves the running result untouched;
+    sq = 0 is a no-op."""
+    say(f"empty blocks: dtype={dtype}")
+    q, q64 = tensor(71, 1, 0, (1, 37, 4, 128), dtype)
+    k0 = torch.empty((1, 0, 2, 128), dtype=dtype, device="cuda")
+    o = torch.full((1, 37, 4, 128), 7.0, device="cuda")
+    lse = torch.full((1, 37, 4), 7.0, device="cuda")
+    cls = ra.ring_attn_step(q, k0, k0, o, lse, 0, 0, True, 0.1, accumulate=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q64, np.zeros((1, 0, 2, 128)), np.zeros((1, 0, 2, 128)),
+                                          np.arange(37), np.arange(0), True, 0.1)
+    assert cls == ra.SKIP == oracle.classify_ref(0, 37, 0, 0, True)
+    assert np.array_equal(host64(o), o_ref) and np.array_equal(host64(lse), lse_ref)
+    o.fill_(3.0)
+    lse.fill_(2.0)
+    ra.ring_attn_step(q, k0, k0, o, lse, 0, 0, True, 0.1, accumulate=True)
+    torch.cuda.synchronize()
+    assert bool((o == 3.0).all()) and bool((lse == 2.0).all())
+    k, _ = tensor(71, 2, 0, (1, 50, 2, 128), dtype)
+    q0 = torch.empty((1, 0, 4, 128), dtype=dtype, device="cuda")
+    o0 = torch.empty((1, 0, 4, 128), device="cuda")
+    l0 = torch.empty((1, 0, 4), device="cuda")
+    ra.ring_attn_step(q0, k, k, o0, l0, 0, 0, True, 0.1, accumulate=False)
+    torch.cuda.synchronize()
+
+
 def test_deterministic(ra):
     q, _ = tensor(8, 1, 0, (1, 300, 4, 128), torch.bfloat16)
     k, _ = tensor(8, 2, 0, (1, 500, 2, 128), torch.bfloat16)
