@@ -18,8 +18,9 @@
 //  * workgroup = 4 waves = 128 query rows of one (job, batch, query head);
 //    each wave owns 32 rows whose Q fragment stays in registers for the
 //    sweep; grids under two workgroups per CU use 8 waves (two key-split
-//    halves merged through LDS), and a complementary two-job step can pair
-//    two query tiles in one workgroup;
+//    halves merged through LDS), grids with at least two 256-row
+//    workgroups per CU use 8 waves on 256 rows sharing every K/V tile, and a
+//    complementary two-job step can pair two query tiles in one workgroup;
 //  * K/V tiles of 64 keys go HBM -> LDS with bounded buffer loads (one
 //    descriptor per segment, the tile offset in soffset; rows past a segment
 //    read as zero), two stages each, XOR-swizzled 16-byte chunks for
@@ -30,6 +31,8 @@
 //  * P^T stays in registers and is the B operand of O^T += V^T P^T; the
 //    contraction order over keys is permuted to match the score layout, and
 //    V^T is read with ds_read_b64_tr_b16 from row-major V in LDS;
+//  * the next tile's S^T MFMAs are interleaved with this tile's
+//    exponentials, then P V runs with its LDS reads kept ahead of the MFMAs;
 //  * exp2-domain online softmax with a lazily raised running max; tiles that
 //    need no mask skip it with one compare.
 #include <hip/hip_runtime.h>
@@ -164,8 +167,6 @@ struct Bf16Cfg {
   static constexpr int VTILE = kBN * DV;             // bf16 elements of one V stage
   static constexpr int KDMA = kBN * KCPR / kThreads;  // 16-B direct loads per thread per K tile
   static constexpr int VDMA = kBN * VCPR / kThreads;
-  static constexpr int KROWS_PER_DMA = kThreads / KCPR;  // K rows one block-wide direct load fills
-  static constexpr int VROWS_PER_DMA = kThreads / VCPR;
   static constexpr int QC = DQK / 16;  // MFMA steps of S^T = K Q^T
   static constexpr int DB = DV / 32;   // 32-row d_v blocks of O^T
   static_assert(KDMA * kThreads == kBN * KCPR && VDMA * kThreads == kBN * VCPR, "tile split");
