@@ -95,6 +95,35 @@ def test_skip_pair_writes_identity_or_nothing(ra):
     assert torch.all(o == 0.0) and torch.all(torch.isneginf(lse))
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes across every supported head-dim pair, GQA group,
+    causal offset (FULL / DIAG / partly empty rows), batch and ragged size."""
+    rng = np.random.default_rng(seed)
+    pairs = [(64, 64), (128, 128), (192, 128)]
+    out = []
+    for i in range(n):
+        dqk, dv = pairs[i % 3]
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.choice([1, 1, 2]))
+        sq = int(rng.integers(1, 300))
+        sk = int(rng.integers(1, 400))
+        causal = bool(rng.integers(0, 2))
+        q0 = int(rng.integers(0, 600))
+        k0 = int(rng.integers(0, 600))
+        out.append((B, sq, sk, hq, hkv, dqk, dv, q0, k0, causal))
+    return out
+
+
+RANDOM_CASES = _random_cases(24, 2026)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM_CASES)))
+def test_ring_attn_step_random_shapes(ra, idx):
+    """bf16 ring step on seeded random shapes, accumulate alternating."""
+    _run_case(ra, 200 + idx, RANDOM_CASES[idx], torch.bfloat16, accumulate=bool(idx % 2))
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_empty_key_and_query_blocks(ra, dtype):
     """sk = 0: a non-accumulating step writes O = 0 and LSE = -inf (the oracle
