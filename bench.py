@@ -56,6 +56,8 @@ def parse():
                    help="only run the sharded decode kernel K times (for counter passes)")
     p.add_argument("--merge-only", type=int, default=0, metavar="K",
                    help="only run the standalone LSE merge K times (for counter passes)")
+    p.add_argument("--long-step-only", type=int, default=0, metavar="K",
+                   help="only run one FULL ring-step launch of the 1M-token prefill K times")
     return p.parse_args()
 
 
@@ -181,7 +183,7 @@ def time_steps(step_fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def profiled_traffic(summary, source):
+def profiled_traffic(summary, source, field="traffic_bytes_per_launch"):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when the kernel source changed after the counters were taken."""
     import hashlib
@@ -194,10 +196,10 @@ def profiled_traffic(summary, source):
     sha = hashlib.sha256(src).hexdigest()[:16]
     key = f"kernel source sha256 prefix ({source})"
     fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and
-                  line.split(": ", 1)[0] in (key, "traffic_bytes_per_launch"))
-    if fields.get(key, "").strip() != sha:
+                  line.split(": ", 1)[0] in (key, field))
+    if fields.get(key, "").strip() != sha or field not in fields:
         return None
-    return int(float(fields["traffic_bytes_per_launch"]))
+    return int(float(fields[field]))
 
 
 def roofline_entry(bound, achieved, peak, unit, traffic=None):
@@ -366,6 +368,21 @@ def merge_bench(steps, warmup):
     return sec, nbytes
 
 
+def long_step_only(reps):
+    """One FULL ring step of the 1M-token zigzag prefill (rank 0, cp 8): the
+    launch that attends the tail query part to a whole staged block and
+    forwards the next one, K times, for counter passes."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.zigzag_setup(4)
+    fn = zigzag_launches(w, ra.FULL)[0]
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"long_step_launches": reps}), flush=True)
+
+
 def merge_only(reps):
     """The standalone LSE merge alone, K launches, for counter passes."""
     import torch
@@ -426,6 +443,9 @@ def main():
     if args.merge_only:
         merge_only(args.merge_only)
         return
+    if args.long_step_only:
+        long_step_only(args.long_step_only)
+        return
 
     log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
     w2, sec2, l2 = zigzag_bench(2, args.steps, args.warmup)
@@ -471,7 +491,10 @@ def main():
                 "value": round(w4["flops"] / s4 / 1e12, 3), "unit": "TFLOP/s",
                 "ms_per_step": round(s4 * 1e3, 3), "flops_per_step": w4["flops"],
                 "roofline": roofline_entry("mfma", l4["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
-                "full_pair_ms": round(l4["full_ms"], 3), "diag_pair_ms": round(l4["diag_ms"], 3)}
+                "full_pair_ms": round(l4["full_ms"], 3), "diag_pair_ms": round(l4["diag_ms"], 3),
+                "full_step_traffic_bytes": profiled_traffic(
+                    "attn_step_bf16_long_prefill_1M_cp8_full_step.md", "attn_step.hip",
+                    field="full_step_traffic_bytes_per_launch")}
             del w4
             torch.cuda.empty_cache()
         if not only or "c3" in only:
