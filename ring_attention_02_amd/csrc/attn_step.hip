@@ -113,6 +113,7 @@ struct JobArgs {
   int32_t n_jobs, hq, hkv, group;
   int32_t n_qtiles, total_wgs;
   int32_t causal, reverse_q;
+  int32_t serp_w;   // > 0: workgroups of odd rounds of serp_w per XCD sweep keys backwards
   float scale, scale_log2;
 };
 struct VarlenArgs {
@@ -291,6 +292,10 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // diagonal step): item 0 is query tile p of job 0, item 1 is tile
   // n_qtiles-1-p of job 1, run one after the other.
   const int logical = xcd_contiguous_id(blockIdx.x, a.total_wgs);
+  // Serpentine key order: the workgroups an XCD runs together sweep a kv
+  // head's tiles in step and share its L2; one that starts after another
+  // finished sweeps the other way, from where the running ones still are.
+  const bool rev = a.serp_w > 0 && ((blockIdx.x / 8) / a.serp_w) % 2 == 1;
   int jb0, qt0, rest;
   if constexpr (PAIRED) {
     jb0 = 0;
@@ -390,6 +395,10 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // Moves a cursor (segment sg covering virtual tiles [start, end)) forward
   // to the segment that holds virtual tile vt < ntiles.
   auto advance = [&](int& sg, int& start, int& end, int vt) {
+    if (vt < start) {   // a backward sweep left the segment: start over
+      sg = -1;
+      start = end = 0;
+    }
     while (vt >= end && sg < kMaxSegs - 1) {
       ++sg;
       start = end;
@@ -456,18 +465,21 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
     const int width = is_k ? DQK : DV;
     const uint16_t* base = seg_base(c.sg, is_k) + (static_cast<int64_t>(b) * sk * a.hkv + kvh) * width;
-    const int64_t key0 = static_cast<int64_t>(vt - c.start) * kBN;
+    // a backward sweep bases the descriptor below vt so the next tiles reuse it
+    const int rebase = is_k ? rebase_k : rebase_v;
+    const int base_vt = rev ? max(c.start, vt - rebase + 1) : vt;
+    const int64_t key0 = static_cast<int64_t>(base_vt - c.start) * kBN;
     // bytes from the base tile to the end of key sk-1's row of this head
     const int64_t valid = ((sk - 1 - key0) * row_elems + width) * 2;
     const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
-    c.base_vt = vt;
+    c.base_vt = base_vt;
     c.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
                                                static_cast<short>(0), nrec, 0x00020000);
   };
   const auto no_rsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(nullptr), static_cast<short>(0), 0, 0);
   DmaCursor kcur{-1, 0, 0, 0, no_rsrc}, vcur{-1, 0, 0, 0, no_rsrc};
   auto dma_k = [&](int vt, int stage) {
-    if (vt >= kcur.end || vt - kcur.base_vt >= rebase_k) seek(kcur, vt, true);
+    if (vt >= kcur.end || vt < kcur.base_vt || vt - kcur.base_vt >= rebase_k) seek(kcur, vt, true);
     const int soff = (vt - kcur.base_vt) * tile_bytes_k;
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
@@ -477,7 +489,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
           static_cast<int>(koffb[i]), soff, 0, 0);
   };
   auto dma_v = [&](int vt, int stage) {
-    if (vt >= vcur.end || vt - vcur.base_vt >= rebase_v) seek(vcur, vt, false);
+    if (vt >= vcur.end || vt < vcur.base_vt || vt - vcur.base_vt >= rebase_v) seek(vcur, vt, false);
     const int soff = (vt - vcur.base_vt) * tile_bytes_v;
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
@@ -541,7 +553,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   };
   MaskCursor mcur{-1, 0, 0, 0, 0, 0};
   auto mask_tile = [&](int vt, f32x16* s) {
-    if (vt >= mcur.end) {
+    if (vt >= mcur.end || vt < mcur.start) {
       advance(mcur.sg, mcur.start, mcur.end, vt);
       mcur.sk = seg_sk(mcur.sg);
       mcur.k_pos0 = seg_kpos0(mcur.sg);
@@ -587,7 +599,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // fewer tiles idles through its last one.
   const int my_n = ntiles > half ? (ntiles - half + SPLIT - 1) / SPLIT : 0;
   const int n_iter = (ntiles + SPLIT - 1) / SPLIT;
-  auto tile = [&](int j) { return j * SPLIT + half; };
+  auto tile = [&](int j) { return rev ? ntiles - 1 - (j * SPLIT + half) : j * SPLIT + half; };
   // Online softmax of tile j (exp2 domain) plus the scores of tile j+1 on
   // MFMA interleaved with the exponentials.  The next scores are computed
   // even after the last tile (from a stale stage, then dropped): with no
@@ -914,8 +926,10 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
   args.total_wgs = static_cast<int32_t>(total);
   if (args.n_fwd > 0) args.fwd_per_wg = (args.fwd_end[kMaxFwd - 1] + total - 1) / total;
   const dim3 grid(static_cast<unsigned>(total));
+  const int xcd_cus = std::max(1, device_cus() / 8);
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
+      args.serp_w = xcd_cus;   // one 8-wave workgroup per CU
       if (args.paired)
         hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true, false>), grid, dim3(2 * kThreads), 0,
                            stream, args);
@@ -934,10 +948,12 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
   if (total_wide >= 2 * static_cast<int64_t>(device_cus())) {
     args.n_qtiles = static_cast<int32_t>(n_wide);
     args.total_wgs = static_cast<int32_t>(total_wide);
+    args.serp_w = xcd_cus;       // one 8-wave workgroup per CU
     if (args.n_fwd > 0) args.fwd_per_wg = (args.fwd_end[kMaxFwd - 1] + total_wide - 1) / total_wide;
     hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2>), dim3(static_cast<unsigned>(total_wide)),
                        dim3(2 * kThreads), 0, stream, args);
   } else {
+    args.serp_w = 2 * xcd_cus;   // two 4-wave workgroups per CU
     hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
   }
   const hipError_t err = hipGetLastError();
@@ -957,8 +973,10 @@ int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   args.base.n_qtiles = static_cast<int32_t>(n_qtiles);
   args.base.total_wgs = static_cast<int32_t>(total);
   const dim3 grid(static_cast<unsigned>(total));
+  const int xcd_cus = std::max(1, device_cus() / 8);
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
+      args.base.serp_w = xcd_cus;
       hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, true>), grid, dim3(2 * kThreads), 0,
                          stream, args);
       const hipError_t err = hipGetLastError();
@@ -968,6 +986,7 @@ int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   }
   // (128-row tiles here: packed requests end on ragged rows, which 256-row
   // tiles waste -- measured slower for the varlen mix.)
+  args.base.serp_w = 2 * xcd_cus;
   hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, true>), grid, dim3(kThreads), 0, stream, args);
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));
