@@ -669,3 +669,40 @@ def test_allgather_kv_reorg_then_segmented_prefill(ra):
     ro, rl = oracle.attention_ref(q64, k64s[r][None], v64s[r][None], L - sq + np.arange(sq), np.arange(L),
                                   True)
     compare(host64(o), host64(lse), ro, rl, BF16_O, BF16_LSE, "reorganised chunk")
+
+
+# Launch shapes that give an XCD more than one round of workgroups, so the
+# workgroups of odd rounds sweep their keys backwards (serpentine order):
+# the 8-wave key-split mode (288 workgroups), the 4-wave mode (768) and the
+# 256-row mode (1,024), causal with a diagonal and ragged tails.  The oracle
+# runs on a few heads of each.
+SERPENTINE = [
+    # (sq, sk, hq, hkv, dqk, dv, q_pos0, k_pos0)
+    (384, 700, 96, 96, 128, 128, 300, 0),      # 8-wave key split, 2 rounds
+    (768, 650, 128, 16, 64, 64, 400, 100),     # 4-wave, 2 rounds
+    (1000, 520, 256, 32, 128, 128, 200, 0),    # 256-row, 4 rounds, ragged rows
+    (1000, 300, 256, 256, 192, 128, 250, 100), # 256-row d 192
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SERPENTINE)))
+def test_serpentine_rounds_match_oracle(ra, idx):
+    sq, sk, hq, hkv, dqk, dv, q0, k0 = SERPENTINE[idx]
+    say(f"serpentine case {idx}: sq={sq} sk={sk} hq={hq} hkv={hkv} d=({dqk},{dv}) q0={q0} k0={k0}")
+    cfg = 300 + idx
+    q, q64 = tensor(cfg, 1, 0, (1, sq, hq, dqk), torch.bfloat16)
+    k, k64 = tensor(cfg, 2, 0, (1, sk, hkv, dqk), torch.bfloat16)
+    v, v64 = tensor(cfg, 3, 0, (1, sk, hkv, dv), torch.bfloat16)
+    o = torch.empty((1, sq, hq, dv), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    scale = 1.0 / np.sqrt(dqk)
+    ra.ring_attn_step(q, k, v, o, lse, q0, k0, True, scale, accumulate=False)
+    torch.cuda.synchronize()
+    o_h, lse_h = host64(o), host64(lse)
+    group = hq // hkv
+    for h in sorted({0, 1, hq // 2 + 3, hq - 1}):
+        o_ref, lse_ref = oracle.attention_ref(q64[:, :, h:h + 1], k64[:, :, h // group:h // group + 1],
+                                              v64[:, :, h // group:h // group + 1], q0 + np.arange(sq),
+                                              k0 + np.arange(sk), True, scale)
+        compare(o_h[:, :, h:h + 1], lse_h[:, :, h:h + 1], o_ref, lse_ref, BF16_O, BF16_LSE,
+                f"serpentine {idx} head {h}")
