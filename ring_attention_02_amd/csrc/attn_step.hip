@@ -319,7 +319,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   const int b = rest / a.hq;
   const int kvh = h / a.group;
   if (a.n_fwd > 0) fwd.store_first_and_rest(a, blockIdx.x, tid);
-#pragma unroll 1
+#pragma unroll
   for (int item = 0; item < (PAIRED ? 2 : 1); ++item) {
   if (item > 0) __syncthreads();   // the previous item is done with the LDS stages
   const int jb = item == 0 ? jb0 : 1;
@@ -608,10 +608,12 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // row share m_run.  It is raised only when some row of the wave gained more
   // than tau (log2 units); otherwise the stale max stays, which is exact
   // because numerator and denominator share it, and P stays below 2^tau.
-  // Fast form (d_qk <= 128, unpaired): next scores always computed and the
-  // loop unrolled by two so the score buffers swap without copies.  The
-  // other kernels keep a branch and a copy: there the unrolled body spills.
-  constexpr bool kAlwaysNext = DQK <= 128 && !PAIRED;
+  // Fast form (d_qk <= 128): next scores always computed and the loop
+  // unrolled by two so the score buffers swap without copies (paired
+  // kernels also unroll their two work items, which keeps them free of
+  // spills).  The d_qk = 192 kernels keep a branch and a copy: there the
+  // unrolled body spills.
+  constexpr bool kAlwaysNext = DQK <= 128;
   auto softmax_and_next_scores = [&](int j, f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, int next_stage) {
     mask_tile(tile(j), s_cur);
     float mx = kNegInf;
