@@ -191,10 +191,11 @@ __device__ __forceinline__ int vswz(int c, int r) {
 
 // This workgroup's slice of the forwarded ranges: 16-byte units
 // [wg * fwd_per_wg, ...) of their concatenation.  The first round (four units
-// per thread) is split in two so its loads can be issued before the
-// prologue's K/V loads and its stores after them; any further rounds run
-// range by range.  Lanes past the end load an in-bounds unit and store
-// nothing, so the loads need no branches.
+// per thread) is split in two: its loads are issued on entry and its stores
+// after the workgroup has mapped itself to its work, before the prologue's
+// own loads (issuing those first was measured slower on long launches); any
+// further rounds run range by range.  Lanes past the end load an in-bounds
+// unit and store nothing, so the loads need no branches.
 template <int NT>
 struct FwdSlice {
   u32x4 x[4];
@@ -261,8 +262,11 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   const JobArgs& a = base_args(args);
   using C = Bf16Cfg<DQK, DV>;
-  // K stages of both halves, then V stages of both halves.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SPLIT * 2 * (C::KTILE + C::VTILE)];
+  // K stages of both halves, then V stages of both halves; after the sweep
+  // the key-split halves swap their states through the same memory.
+  constexpr int kStageElems = SPLIT * 2 * (C::KTILE + C::VTILE);
+  constexpr int kSwapElems = SPLIT == 2 ? 8 * (16 * (C::DB / 2) + 2) * 64 * 2 : 0;   // floats as uint16 pairs
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStageElems > kSwapElems ? kStageElems : kSwapElems];
   uint16_t* const Ks = smem;
   uint16_t* const Vs = smem + SPLIT * 2 * C::KTILE;
 
@@ -700,65 +704,97 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     }
   }
 
-  if constexpr (SPLIT == 2) {
-    // Fold the odd-tile half into the even-tile half, lane by lane (same query
-    // row, same key half hh): the K/V stages are free now and hold the states.
-    __syncthreads();
-    float* xs = reinterpret_cast<float*>(smem);   // [wave][16*DB + 2][64 lanes]
-    constexpr int NV = 16 * C::DB + 2;
-    static_assert(4 * NV * 64 * sizeof(float) <= sizeof(smem), "merge buffer fits the stages");
-    float* mine = xs + wave * NV * 64 + lane;
-    if (half == 1) {
+  // ---- epilogue: normalise, LSE, optional merge into the running result.
+  // In the key-split variant each half finalises half of the d_v blocks
+  // (half 0 the low ones), after the two halves have swapped the other
+  // blocks and their (max, sum) through LDS; so all eight waves store.  The
+  // running result of an accumulating launch is fetched before that swap,
+  // so its latency hides behind it.
+  constexpr int DH = SPLIT == 2 ? C::DB / 2 : C::DB;   // d_v blocks this wave finalises
+  static_assert(DH * SPLIT == C::DB, "d_v blocks split evenly between the halves");
+  const int64_t orow = (static_cast<int64_t>(b) * sq + (row_valid ? my_row : 0)) * a.hq + h;
+  float* const op = j_o() + orow * DV + half * DH * 32;   // first column of my blocks
+  const bool acc = job.accumulate != 0;
+  float lse_old = kNegInf;
+  f32x4 o_old[DH * 4];
+  auto load_old = [&]() {
+    if (!acc || !row_valid) return;
+    lse_old = j_lse()[orow];
 #pragma unroll
-      for (int d = 0; d < C::DB; ++d)
+    for (int dd = 0; dd < DH; ++dd)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mine[(16 * d + i) * 64] = oacc[d][i];
-      mine[(NV - 2) * 64] = m_run;
-      mine[(NV - 1) * 64] = l_run;
-    }
-    __syncthreads();
-    if (half == 0) {
-      const float m1 = mine[(NV - 2) * 64];
-      const float l1 = mine[(NV - 1) * 64];
+      for (int j = 0; j < 4; ++j) o_old[4 * dd + j] = *reinterpret_cast<const f32x4*>(op + dd * 32 + 8 * j + 4 * hh);
+  };
+  // (The paired kernel reads it at the stores: held across the swap, it spills.)
+  constexpr bool kEarlyOld = !PAIRED;
+  if constexpr (kEarlyOld) load_old();
+  // Swap buffer of the key-split halves, lane by lane (the same query row
+  // and key half hh in both waves): [wave_all][16*DH + 2][64 lanes].
+  constexpr int NV = 16 * DH + 2;
+  static_assert(SPLIT == 1 || 8 * NV * 64 * sizeof(float) <= sizeof(smem), "swap buffer fits the stages");
+  float* const mine = reinterpret_cast<float*>(smem) + wave_all * NV * 64 + lane;
+  const float* const theirs = reinterpret_cast<const float*>(smem) + (wave_all ^ 4) * NV * 64 + lane;
+  // Register blocks are indexed with constants only: H is this wave's half.
+  auto swap_out = [&](auto hc) {
+    constexpr int P0 = (1 - decltype(hc)::value) * DH;   // the partner's blocks
+#pragma unroll
+    for (int dd = 0; dd < DH; ++dd)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mine[(16 * dd + i) * 64] = oacc[P0 + dd][i];
+    mine[(NV - 2) * 64] = m_run;
+    mine[(NV - 1) * 64] = l_run;
+  };
+  auto finish = [&](auto hc) {
+    constexpr int H = decltype(hc)::value;
+    constexpr int D0 = H * DH;   // my blocks
+    if constexpr (SPLIT == 2) {
+      const float m1 = theirs[(NV - 2) * 64];
+      const float l1 = theirs[(NV - 1) * 64];
       const float m = fmaxf(m_run, m1);
       const float m_use = m == kNegInf ? 0.f : m;
       const float a0 = fast_exp2((m_run - m_use) * a.scale_log2);   // 0 for an empty side
       const float a1 = fast_exp2((m1 - m_use) * a.scale_log2);
 #pragma unroll
-      for (int d = 0; d < C::DB; ++d)
+      for (int dd = 0; dd < DH; ++dd)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] = oacc[d][i] * a0 + mine[(16 * d + i) * 64] * a1;
+        for (int i = 0; i < 16; ++i) oacc[D0 + dd][i] = oacc[D0 + dd][i] * a0 + theirs[(16 * dd + i) * 64] * a1;
       l_run = l_run * a0 + l1 * a1;
       m_run = m;
     }
-  }
-
-  // ---- epilogue (the even half): normalise, LSE, optional merge into the
-  // running result
-  if (row_valid && half == 0) {
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool has = m_run != kNegInf && l_tot > 0.f;
-  const float inv = has ? 1.f / l_tot : 0.f;
-  const float lse_blk = has ? m_run * a.scale + fast_log2(l_tot) * kLn2 : kNegInf;
-  const int64_t orow = (static_cast<int64_t>(b) * sq + my_row) * a.hq + h;
-  float* op = j_o() + orow * DV;
-  float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
-  if (job.accumulate) lse_out = merge_weights(j_lse()[orow], lse_blk, &w_old, &w_blk);
-  const float wb = w_blk * inv;
-#pragma unroll
-  for (int d = 0; d < C::DB; ++d)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int dv0 = d * 32 + 8 * j + 4 * hh;
-      f32x4 val = {oacc[d][4 * j] * wb, oacc[d][4 * j + 1] * wb, oacc[d][4 * j + 2] * wb,
-                   oacc[d][4 * j + 3] * wb};
-      if (job.accumulate) {
-        const f32x4 old = *reinterpret_cast<const f32x4*>(op + dv0);
-        val += old * w_old;
-      }
-      *reinterpret_cast<f32x4*>(op + dv0) = val;
+    if (!row_valid) return;
+    if constexpr (!kEarlyOld) {
+      if (acc) lse_old = j_lse()[orow];
     }
-  if (hh == 0) j_lse()[orow] = lse_out;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const bool has = m_run != kNegInf && l_tot > 0.f;
+    const float inv = has ? 1.f / l_tot : 0.f;
+    const float lse_blk = has ? m_run * a.scale + fast_log2(l_tot) * kLn2 : kNegInf;
+    float w_old = 0.f, w_blk = 1.f, lse_out = lse_blk;
+    if (acc) lse_out = merge_weights(lse_old, lse_blk, &w_old, &w_blk);
+    const float wb = w_blk * inv;
+#pragma unroll
+    for (int dd = 0; dd < DH; ++dd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& oa = oacc[D0 + dd];
+        f32x4 val = {oa[4 * j] * wb, oa[4 * j + 1] * wb, oa[4 * j + 2] * wb, oa[4 * j + 3] * wb};
+        if (acc) {
+          if constexpr (kEarlyOld) val += o_old[4 * dd + j] * w_old;
+          else val += *reinterpret_cast<const f32x4*>(op + dd * 32 + 8 * j + 4 * hh) * w_old;
+        }
+        *reinterpret_cast<f32x4*>(op + dd * 32 + 8 * j + 4 * hh) = val;
+      }
+    if (H == 0 && hh == 0) j_lse()[orow] = lse_out;
+  };
+  if constexpr (SPLIT == 2) {
+    __syncthreads();   // every wave is done with the K/V stages
+    if (half == 0) swap_out(std::integral_constant<int, 0>{});
+    else swap_out(std::integral_constant<int, 1>{});
+    __syncthreads();
+    if (half == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
+  } else {
+    finish(std::integral_constant<int, 0>{});
   }
   }   // work items
 #endif

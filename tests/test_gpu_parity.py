@@ -453,32 +453,46 @@ def test_jobs_forward_without_attention_work(ra):
     assert bool((o == 5.0).all()) and bool((lse == 2.0).all())
 
 
-def test_jobs_paired_diagonal_step(ra):
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_jobs_paired_diagonal_step(ra, accumulate):
     """The head-tail diagonal step in one launch: job 0 = the head part over its
     own chunk (DIAG), job 1 = the tail part over the head chunk (FULL) and its
     own chunk (DIAG).  With 64 heads and 4 query tiles the plain grid is 512
     workgroups, so on a 256-CU device the launch pairs tile p of job 0 with
-    tile 3-p of job 1 in one 8-wave workgroup; results must not change."""
-    c, hq, d = 512, 64, 128
+    tile 3-p of job 1 in one 8-wave workgroup; results must not change.
+    With accumulate, both jobs merge into a partial over 96 earlier keys."""
+    c, hq, d, pre = 512, 64, 128, 96
     q, _ = tensor(91, 1, 0, (1, 2 * c, hq, d), torch.bfloat16)
     k, _ = tensor(91, 2, 0, (1, 2 * c, hq, d), torch.bfloat16)
     v, _ = tensor(91, 3, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    k_pre, _ = tensor(91, 4, 0, (1, pre, hq, d), torch.bfloat16)
+    v_pre, _ = tensor(91, 5, 0, (1, pre, hq, d), torch.bfloat16)
     o = torch.empty((1, 2 * c, hq, d), device="cuda")
     lse = torch.empty((1, 2 * c, hq), device="cuda")
-    tail0 = 7 * c        # positions: head part 0..c-1, tail part 7c..8c-1
+    # positions: earlier keys 0..pre-1, head part pre.., tail part pre+7c..
+    head0, tail0 = pre, pre + 7 * c
     k_head, v_head = k[:, :c].contiguous(), v[:, :c].contiguous()
     k_tail, v_tail = k[:, c:].contiguous(), v[:, c:].contiguous()
-    jobs = [dict(q=q[:, :c], o=o[:, :c], lse=lse[:, :c], q_pos0=0, accumulate=False,
-                 segments=[(k_head, v_head, 0)]),
-            dict(q=q[:, c:], o=o[:, c:], lse=lse[:, c:], q_pos0=tail0, accumulate=False,
-                 segments=[(k_head, v_head, 0), (k_tail, v_tail, tail0)])]
+    if accumulate:
+        for part, q0 in ((slice(0, c), head0), (slice(c, 2 * c), tail0)):
+            ra.ring_attn_step(q[:, part], k_pre, v_pre, o[:, part], lse[:, part], q_pos0=q0,
+                              k_pos0=0, causal=True)
+    jobs = [dict(q=q[:, :c], o=o[:, :c], lse=lse[:, :c], q_pos0=head0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0)]),
+            dict(q=q[:, c:], o=o[:, c:], lse=lse[:, c:], q_pos0=tail0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0), (k_tail, v_tail, tail0)])]
     ra.ring_attn_step_jobs(jobs, causal=True)
     torch.cuda.synchronize()
     heads = [0, 17, 63]
     q64 = host64(q)[:, :, heads]
     k64, v64 = host64(k)[:, :, heads], host64(v)[:, :, heads]
-    pos = np.concatenate([np.arange(c), tail0 + np.arange(c)])
-    ro, rl = oracle.attention_ref(q64, k64, v64, pos, pos, True)
+    pos = np.concatenate([head0 + np.arange(c), tail0 + np.arange(c)])
+    kpos = pos
+    if accumulate:
+        k64 = np.concatenate([host64(k_pre)[:, :, heads], k64], 1)
+        v64 = np.concatenate([host64(v_pre)[:, :, heads], v64], 1)
+        kpos = np.concatenate([np.arange(pre), pos])
+    ro, rl = oracle.attention_ref(q64, k64, v64, pos, kpos, True)
     compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE, "paired")
 
 
