@@ -979,17 +979,29 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
       return CP_OK;
     }
   }
-  RA_CHECK(!args.paired, CP_EUNSUPPORTED, "ring_attn_step: paired launch needs the 8-wave variant");
-  // Large grids: 256-row workgroups while that still leaves two per CU.
+  // Large grids: 256-row workgroups while that still leaves two per CU
+  // (paired launches: 256-row tile p of job 0, then tile n-1-p of job 1).
   const int64_t n_wide = (args.sq + 2 * kBM - 1) / (2 * kBM);
-  const int64_t total_wide = n_wide * args.n_jobs * args.hq * batch;
+  const int64_t total_wide = n_wide * (args.paired ? 1 : args.n_jobs) * args.hq * batch;
+  RA_CHECK(!args.paired || (DQK <= 128 && total_wide >= 2 * static_cast<int64_t>(device_cus())),
+           CP_EUNSUPPORTED, "ring_attn_step: no paired variant for this grid");
   if (total_wide >= 2 * static_cast<int64_t>(device_cus())) {
     args.n_qtiles = static_cast<int32_t>(n_wide);
     args.total_wgs = static_cast<int32_t>(total_wide);
     args.serp_w = xcd_cus;       // one 8-wave workgroup per CU
     if (args.n_fwd > 0) args.fwd_per_wg = (args.fwd_end[kMaxFwd - 1] + total_wide - 1) / total_wide;
-    hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2>), dim3(static_cast<unsigned>(total_wide)),
-                       dim3(2 * kThreads), 0, stream, args);
+    const dim3 wide(static_cast<unsigned>(total_wide));
+    bool launched = false;
+    if constexpr (DQK <= 128) {
+      if (args.paired) {
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, true, false, 2>), wide, dim3(2 * kThreads), 0,
+                           stream, args);
+        launched = true;
+      }
+    }
+    if (!launched)
+      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2>), wide, dim3(2 * kThreads), 0,
+                         stream, args);
   } else {
     args.serp_w = 2 * xcd_cus;   // two 4-wave workgroups per CU
     hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
@@ -1042,11 +1054,12 @@ bool head_dims_ok(int32_t d_qk, int32_t d_v) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-// Key tiles of one query tile of a job: the tiles of each segment that its
-// last row can see (the kernel's sweep length for that workgroup).
-int job_tiles(const JobArgs& ja, int j, int64_t qt) {
+// Key tiles of one query tile (of `rows` rows) of a job: the tiles of each
+// segment that its last row can see (the kernel's sweep length for that
+// workgroup).
+int job_tiles(const JobArgs& ja, int j, int64_t qt, int64_t rows = kBM) {
   const QJob& jb = ja.job[j];
-  const int64_t q_last = std::min(ja.sq, (qt + 1) * kBM) - 1;
+  const int64_t q_last = std::min(ja.sq, (qt + 1) * rows) - 1;
   int tiles = 0;
   for (int sg = 0; sg < jb.n_seg; ++sg) {
     int64_t nkeys = jb.seg[sg].sk;
@@ -1057,15 +1070,33 @@ int job_tiles(const JobArgs& ja, int j, int64_t qt) {
 }
 
 // Should a two-job launch pair query tile p of job 0 with tile n-1-p of job 1
-// in one workgroup?  Only grids of at most one workgroup per CU slot are
-// considered (larger grids balance themselves as workgroups retire), and the
-// paired grid must run as 8-wave workgroups.  Cost model in tiles at a full
-// CU: an 8-wave workgroup (fewer workgroups than two per CU) owns its CU, a
-// 4-wave one shares it with another.
+// in one workgroup?
+//  * Grids of at most one workgroup per CU slot: when the pairs' cost beats
+//    the plain grid's in a cost model in tiles at a full CU (an 8-wave
+//    workgroup, fewer than two per CU, owns its CU; a 4-wave one shares it);
+//    the paired grid runs as 8-wave key-split workgroups.
+//  * Large grids (256-row workgroups, at least two per CU once paired): when
+//    pairing evens out workgroups whose single loads differ by more than 2x
+//    (every pair within 1/16 of the largest).  The head-tail diagonal step
+//    is such a launch; with equal workgroups the ones an XCD runs together
+//    stay in step and keep sharing its L2.
 bool pairing_pays(const JobArgs& ja, int64_t batch, int d_qk) {
-  if (ja.n_jobs != 2) return false;
-  const int64_t n = (ja.sq + kBM - 1) / kBM;
+  if (ja.n_jobs != 2 || d_qk > 128) return false;
   const int64_t cus = device_cus();
+  const int64_t nw = (ja.sq + 2 * kBM - 1) / (2 * kBM);
+  if (nw * ja.hq * batch >= 2 * cus) {
+    int max_single = 0, min_single = 1 << 30, max_pair = 0, min_pair = 1 << 30;
+    for (int64_t p = 0; p < nw; ++p) {
+      const int a0 = job_tiles(ja, 0, p, 2 * kBM), a1 = job_tiles(ja, 1, p, 2 * kBM);
+      const int pr = a0 + job_tiles(ja, 1, nw - 1 - p, 2 * kBM);
+      max_single = std::max(max_single, std::max(a0, a1));
+      min_single = std::min(min_single, std::min(a0, a1));
+      max_pair = std::max(max_pair, pr);
+      min_pair = std::min(min_pair, pr);
+    }
+    return max_single > 2 * min_single && 16 * (max_pair - min_pair) <= max_pair;
+  }
+  const int64_t n = (ja.sq + kBM - 1) / kBM;
   const int64_t plain_wgs = 2 * n * ja.hq * batch, paired_wgs = n * ja.hq * batch;
   if (plain_wgs > 2 * cus) return false;
   int max_single = 0, max_pair = 0;
@@ -1074,8 +1105,7 @@ bool pairing_pays(const JobArgs& ja, int64_t batch, int d_qk) {
     max_single = std::max(max_single, std::max(a0, a1));
     max_pair = std::max(max_pair, a0 + b1);
   }
-  // pairing runs in the 8-wave variant only
-  if (d_qk > 128 || paired_wgs >= 2 * cus) return false;
+  if (paired_wgs >= 2 * cus) return false;
   const int plain_cost = plain_wgs < 2 * cus ? max_single : 2 * max_single;
   return 20 * max_pair < 17 * plain_cost;
 }

@@ -496,6 +496,48 @@ def test_jobs_paired_diagonal_step(ra, accumulate):
     compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE, "paired")
 
 
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_jobs_paired_diagonal_step_large_grid(ra, accumulate):
+    """The head-tail diagonal step on a large grid: 2048-token parts, 64 query
+    heads over 8 kv heads.  The paired grid is 8 query tiles of 256 rows x 64
+    heads = 512 workgroups (two per CU on a 256-CU device), whose loads the
+    pairing evens out (head tile p sees 4(p+1) key tiles, tail tile 7-p sees
+    32 + 4(8-p)); results must match the oracle on sampled heads."""
+    c, hq, hkv, d, pre = 2048, 64, 8, 128, 96
+    q, _ = tensor(92, 1, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    k, _ = tensor(92, 2, 0, (1, 2 * c, hkv, d), torch.bfloat16)
+    v, _ = tensor(92, 3, 0, (1, 2 * c, hkv, d), torch.bfloat16)
+    k_pre, _ = tensor(92, 4, 0, (1, pre, hkv, d), torch.bfloat16)
+    v_pre, _ = tensor(92, 5, 0, (1, pre, hkv, d), torch.bfloat16)
+    o = torch.empty((1, 2 * c, hq, d), device="cuda")
+    lse = torch.empty((1, 2 * c, hq), device="cuda")
+    head0, tail0 = pre, pre + 7 * c
+    k_head, v_head = k[:, :c].contiguous(), v[:, :c].contiguous()
+    k_tail, v_tail = k[:, c:].contiguous(), v[:, c:].contiguous()
+    if accumulate:
+        for part, q0 in ((slice(0, c), head0), (slice(c, 2 * c), tail0)):
+            ra.ring_attn_step(q[:, part], k_pre, v_pre, o[:, part], lse[:, part], q_pos0=q0,
+                              k_pos0=0, causal=True)
+    jobs = [dict(q=q[:, :c], o=o[:, :c], lse=lse[:, :c], q_pos0=head0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0)]),
+            dict(q=q[:, c:], o=o[:, c:], lse=lse[:, c:], q_pos0=tail0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0), (k_tail, v_tail, tail0)])]
+    ra.ring_attn_step_jobs(jobs, causal=True)
+    torch.cuda.synchronize()
+    heads, kv_heads = [5, 62], [0, 7]            # q-head h reads kv-head h // 8
+    q64 = host64(q)[:, :, heads]
+    k64, v64 = host64(k)[:, :, kv_heads], host64(v)[:, :, kv_heads]
+    pos = np.concatenate([head0 + np.arange(c), tail0 + np.arange(c)])
+    kpos = pos
+    if accumulate:
+        k64 = np.concatenate([host64(k_pre)[:, :, kv_heads], k64], 1)
+        v64 = np.concatenate([host64(v_pre)[:, :, kv_heads], v64], 1)
+        kpos = np.concatenate([np.arange(pre), pos])
+    ro, rl = oracle.attention_ref(q64, k64, v64, pos, kpos, True)
+    compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE,
+            "paired large grid")
+
+
 def _decode_paged_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs, il, spare_blocks,
                        drop=None):
     """Paged caches: each request has its own block table (a random choice of
