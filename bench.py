@@ -22,9 +22,10 @@ Also reported in the same line (unless --primary-only): the long zigzag
 prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
 (GB/s against HBM), the same decode over paged caches read through block
 tables, segmented chunked prefill (MLA shape), a packed multi-request
-(varlen) prefill, the all-gather-KV reorganisation gather and a standalone
-LSE merge, each with the roofline of its dominant kernel, plus the CPU
-oracle timed on the host.
+(varlen) prefill, the all-gather-KV reorganisation gather, the tiny fp32
+non-causal ring (a correctness workload, timed for completeness) and a
+standalone LSE merge, each with the roofline of its dominant kernel, plus
+the CPU oracle timed on the host (all its threads, and on one thread).
 """
 
 import argparse
@@ -37,6 +38,7 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector ALU (published, packed FMA)
 METRIC = "causal attn TFLOP/s per ring-step prefill + decode GB/s, % of roofline"
 
 
@@ -260,6 +262,22 @@ def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
                         per_graph_ms=None if per_graph_sec is None else per_graph_sec * 1e3)
 
 
+def tiny_bench(steps, warmup):
+    """C1: the fp32 non-causal ring, 512 tokens in 4 blocks of 128, 4 heads,
+    d 64: 16 ring-step launches and one 4-part LSE merge per sweep, issued
+    eagerly (a correctness workload: the figure is mostly launch cost)."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    from seeded_inputs import CONFIGS, Q_ID, K_ID, V_ID
+    c = CONFIGS[1]
+    shape = (c["batch"], c["seq"], c["heads"], c["d"])
+    q, k, v = (workloads.host_tensor(1, t, 0, shape, torch.float32) for t in (Q_ID, K_ID, V_ID))
+    flops = c["batch"] * c["seq"] * c["seq"] * c["heads"] * 4 * c["d"]
+    sec = time_steps(lambda: ra.noncausal_ring_sweep(q, k, v, c["n_blocks"]), steps, warmup)
+    return flops, sec
+
+
 def decode_bench(steps, warmup, paged=False):
     import torch
     import ring_attention_02_amd as ra
@@ -416,10 +434,38 @@ def cpu_baseline(w):
         if t_used > budget:
             break
     flops = w["pairs"] * heads_done * (2 * w["d"] + 2 * w["d"])
-    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
-            "kind": "oracle",
-            "sample": f"rank-0 local queries (2048 tokens) x all 8192 keys for {heads_done} of "
-                      f"{w['hq']} heads, float64 numpy, {t_used:.1f} s"}
+    out = {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+           "kind": "oracle",
+           "sample": f"rank-0 local queries (2048 tokens) x all 8192 keys for {heads_done} of "
+                     f"{w['hq']} heads, float64 numpy, {t_used:.1f} s"}
+    # the same oracle on one thread: one head of this workload, and the whole
+    # tiny fp32 ring workload (512 tokens, 4 heads, d 64, no mask)
+    from threadpoolctl import threadpool_limits
+    from seeded_inputs import CONFIGS, Q_ID, K_ID, V_ID
+    c1 = CONFIGS[1]
+    shape1 = (c1["batch"], c1["seq"], c1["heads"], c1["d"])
+    q1, k1, v1 = (workloads.host_tensor(1, t, 0, shape1, torch_f32()).cpu().numpy() for t in (Q_ID, K_ID, V_ID))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.attention_ref(q[None, :, :1], k[None, :, :1], v[None, :, :1], q_pos,
+                             np.arange(k.shape[0]), causal=True)
+        t_head = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.attention_ref(q1, k1, v1, causal=False)
+        t_c1 = time.perf_counter() - t0
+    f_head = w["pairs"] * (2 * w["d"] + 2 * w["d"])
+    f_c1 = c1["batch"] * c1["seq"] * c1["seq"] * c1["heads"] * 4 * c1["d"]
+    out["single_thread"] = {
+        "zigzag_one_head": {"value": round(f_head / t_head / 1e12, 6), "unit": "TFLOP/s",
+                            "seconds": round(t_head, 3)},
+        "tiny_noncausal_ring_f32": {"value": round(f_c1 / t_c1 / 1e12, 6), "unit": "TFLOP/s",
+                                    "seconds": round(t_c1, 4)}}
+    return out
+
+
+def torch_f32():
+    import torch
+    return torch.float32
 
 
 def main():
@@ -548,6 +594,14 @@ def main():
                 "roofline": roofline_entry("hbm", w8["bytes"] / s8 / 1e9, PEAK_HBM_GBS, "GB/s")}
             del w8
             torch.cuda.empty_cache()
+        if not only or "c1" in only:
+            log("C1: tiny non-causal ring, fp32, 512 tokens in 4 blocks")
+            f1, s1 = tiny_bench(max(10, args.steps), 5)
+            sec["tiny_noncausal_ring_f32"] = {
+                "value": round(f1 / s1 / 1e12, 4), "unit": "TFLOP/s", "ms_per_step": round(s1 * 1e3, 4),
+                "flops_per_step": f1,
+                "roofline": roofline_entry("alu", f1 / s1 / 1e12, PEAK_F32_VALU_TFLOPS, "TFLOP/s"),
+                "note": "correctness workload: 16 launches and one merge per sweep, issued eagerly"}
         if not only or "merge" in only:
             log("lse_merge: 2 partials x 8.4M rows x 128")
             s6, b6 = merge_bench(max(5, args.steps), 2)
