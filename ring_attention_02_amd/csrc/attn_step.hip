@@ -306,12 +306,29 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     qt0 = logical % a.n_qtiles;
     rest = logical / a.n_qtiles;
   } else if constexpr (VARLEN) {
-    // query tile fastest, then request (jb0 names the request here)
-    qt0 = logical % a.n_qtiles;
-    rest = logical / a.n_qtiles;
-    jb0 = rest % args.n_req;
-    rest /= args.n_req;
-    if (a.reverse_q) qt0 = a.n_qtiles - 1 - qt0;
+    // (jb0 names the request here)
+    if (a.reverse_q) {
+      // Causal requests: the longest query tiles first across the whole grid
+      // (tile index outermost, descending; a tile's load grows with its
+      // index), then request, then query head within its kv group, kv head
+      // fastest.  Consecutive ids go to consecutive XCDs, so every XCD gets
+      // the same spread of tile lengths, longest first, and with 8 kv heads
+      // keeps to one of them (its q-heads share the XCD's L2).
+      int r = static_cast<int>(blockIdx.x);
+      const int kv = r % a.hkv;
+      r /= a.hkv;
+      const int gq = r % a.group;
+      r /= a.group;
+      jb0 = r % args.n_req;
+      qt0 = a.n_qtiles - 1 - r / args.n_req;
+      rest = kv * a.group + gq;   // the query head (packed requests: batch 0)
+    } else {
+      // query tile fastest, then request
+      qt0 = logical % a.n_qtiles;
+      rest = logical / a.n_qtiles;
+      jb0 = rest % args.n_req;
+      rest /= args.n_req;
+    }
   } else {
     jb0 = logical % a.n_jobs;
     rest = logical / a.n_jobs;
