@@ -527,15 +527,35 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kst + (key * C::KCPR + slot) * 8));
   };
   // One V^T fragment (A operand of O^T += V^T P^T) for d_v block d and
-  // 16-key chunk kc, from row-major V through two transposed LDS reads.
-  auto v_frag = [&](const uint16_t* vst, int d, int kc) -> bf16x8 {
-    const int r0 = kc * 16 + 4 * (g >> 1) + (i16 >> 2);
-    const int r1 = r0 + 8;
+  // 16-key chunk kc, from row-major V through two transposed LDS reads of
+  // rows r0 = 16kc + 4(g/2) + i16/4 and r0 + 8.  The V swizzle reads bits
+  // of r0 that 16kc and +8 leave alone, so each d_v block also has a single
+  // per-lane base, with the chunk, the second read and the stage as constant
+  // offsets.  The d_qk = 192 kernels use that form: it takes the
+  // transposed-read addresses out of the registers their fast loop would
+  // otherwise spill (the d_qk <= 128 kernels measured faster with the
+  // addresses formed per read).
+  constexpr bool kVBase = DQK > 128;
+  int vbase[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) {
+    const int r = 4 * (g >> 1) + (i16 >> 2);
     const int cc = 4 * d + 2 * (g & 1) + ((i16 & 3) >> 1);
-    const int half = 4 * (i16 & 1);
-    const s16x4 lo = lds_read_tr16(vst + (r0 * C::VCPR + vswz<C::VCPR>(cc, r0)) * 8 + half);
-    const s16x4 hi = lds_read_tr16(vst + (r1 * C::VCPR + vswz<C::VCPR>(cc, r1)) * 8 + half);
-    return join_bf16x4(lo, hi);
+    vbase[d] = (r * C::VCPR + vswz<C::VCPR>(cc, r)) * 8 + 4 * (i16 & 1);
+  }
+  auto v_frag = [&](const uint16_t* vst, int d, int kc) -> bf16x8 {
+    if constexpr (kVBase) {
+      const uint16_t* p = vst + vbase[d] + kc * 16 * C::VCPR * 8;
+      return join_bf16x4(lds_read_tr16(p), lds_read_tr16(p + 8 * C::VCPR * 8));
+    } else {
+      const int r0 = kc * 16 + 4 * (g >> 1) + (i16 >> 2);
+      const int r1 = r0 + 8;
+      const int cc = 4 * d + 2 * (g & 1) + ((i16 & 3) >> 1);
+      const int half = 4 * (i16 & 1);
+      const s16x4 lo = lds_read_tr16(vst + (r0 * C::VCPR + vswz<C::VCPR>(cc, r0)) * 8 + half);
+      const s16x4 hi = lds_read_tr16(vst + (r1 * C::VCPR + vswz<C::VCPR>(cc, r1)) * 8 + half);
+      return join_bf16x4(lo, hi);
+    }
   };
   // Scores of a whole tile: s[kb][i] is key 32kb + 8(i/4) + 4hh + i%4.
   auto qk = [&](int stage, f32x16* s) {
@@ -629,12 +649,9 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // row share m_run.  It is raised only when some row of the wave gained more
   // than tau (log2 units); otherwise the stale max stays, which is exact
   // because numerator and denominator share it, and P stays below 2^tau.
-  // Fast form (d_qk <= 128): next scores always computed and the loop
-  // unrolled by two so the score buffers swap without copies (paired
-  // kernels also unroll their two work items, which keeps them free of
-  // spills).  The d_qk = 192 kernels keep a branch and a copy: there the
-  // unrolled body spills.
-  constexpr bool kAlwaysNext = DQK <= 128;
+  // The loop is unrolled by two so the score buffers swap without copies
+  // (paired kernels also unroll their two work items, which keeps them free
+  // of spills).
   auto softmax_and_next_scores = [&](int j, f32x16* s_cur, f32x16* s_nxt, bf16x8* pb, int next_stage) {
     mask_tile(tile(j), s_cur);
     float mx = kNegInf;
@@ -655,18 +672,14 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
       m_run = m_new;
     }
     const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
-    if (kAlwaysNext || j + 1 < my_n) {
-      qk(next_stage, s_nxt);               // MFMA: scores of tile j+1 ...
-      l_run += exps(s_cur, pb, neg_mc);    // ... interleaved with the VALU exponentials of tile j
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    qk(next_stage, s_nxt);               // MFMA: scores of tile j+1 ...
+    l_run += exps(s_cur, pb, neg_mc);    // ... interleaved with the VALU exponentials of tile j
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * C::QC; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
-        if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    } else {
-      l_run += exps(s_cur, pb, neg_mc);
+    for (int i = 0; i < 2 * C::QC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
+      if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
@@ -700,24 +713,9 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
         pv(P, pb);                                     // MFMA: O += P_j V_j
       }
     };
-    if constexpr (kAlwaysNext) {
-      for (int j = 0; j < n_iter; j += 2) {
-        iteration(j, std::integral_constant<int, 0>{}, s_cur, s_nxt);
-        if (j + 1 < n_iter) iteration(j + 1, std::integral_constant<int, 1>{}, s_nxt, s_cur);
-      }
-    } else {
-      for (int j = 0; j < n_iter; ++j) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 2 < my_n) dma_k(tile(j + 2), j & 1);
-        if (j + 1 < my_n) dma_v(tile(j + 1), (j + 1) & 1);
-        if (j < my_n) {
-          softmax_and_next_scores(j, s_cur, s_nxt, pb, (j + 1) & 1);
-          pv(j & 1, pb);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
-      }
+    for (int j = 0; j < n_iter; j += 2) {
+      iteration(j, std::integral_constant<int, 0>{}, s_cur, s_nxt);
+      if (j + 1 < n_iter) iteration(j + 1, std::integral_constant<int, 1>{}, s_nxt, s_cur);
     }
   }
 
