@@ -496,14 +496,16 @@ def test_jobs_paired_diagonal_step(ra, accumulate):
     compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE, "paired")
 
 
-@pytest.mark.parametrize("accumulate", [False, True])
-def test_jobs_paired_diagonal_step_large_grid(ra, accumulate):
+@pytest.mark.parametrize("c,accumulate", [(2048, False), (2048, True), (2200, False)])
+def test_jobs_paired_diagonal_step_large_grid(ra, c, accumulate):
     """The head-tail diagonal step on a large grid: 2048-token parts, 64 query
     heads over 8 kv heads.  The paired grid is 8 query tiles of 256 rows x 64
     heads = 512 workgroups (two per CU on a 256-CU device), whose loads the
     pairing evens out (head tile p sees 4(p+1) key tiles, tail tile 7-p sees
-    32 + 4(8-p)); results must match the oracle on sampled heads."""
-    c, hq, hkv, d, pre = 2048, 64, 8, 128, 96
+    32 + 4(8-p)); results must match the oracle on sampled heads.  2200-token
+    parts give 9 tiles (the middle one meets itself across the two jobs) and
+    a ragged last tile of 152 rows."""
+    hq, hkv, d, pre = 64, 8, 128, 96
     q, _ = tensor(92, 1, 0, (1, 2 * c, hq, d), torch.bfloat16)
     k, _ = tensor(92, 2, 0, (1, 2 * c, hkv, d), torch.bfloat16)
     v, _ = tensor(92, 3, 0, (1, 2 * c, hkv, d), torch.bfloat16)
