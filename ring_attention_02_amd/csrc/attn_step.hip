@@ -672,6 +672,10 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
       m_run = m_new;
     }
     const float neg_mc = -(m_run == kNegInf ? 0.f : m_run) * a.scale_log2;
+    // Raised wave priority over the interleaved block: when both waves of a
+    // SIMD are ready, the one in this block issues first (measured +2 % on
+    // long launches; the same around the PV block gained nothing).
+    __builtin_amdgcn_s_setprio(1);
     qk(next_stage, s_nxt);               // MFMA: scores of tile j+1 ...
     l_run += exps(s_cur, pb, neg_mc);    // ... interleaved with the VALU exponentials of tile j
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -681,6 +685,7 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
       __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::QC), 0);
       if (i + 2 < 2 * C::QC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // prologue: K of this half's tiles 0 and 1 and V of tile 0 in flight
