@@ -540,6 +540,61 @@ def test_jobs_paired_diagonal_step_large_grid(ra, c, accumulate):
             "paired large grid")
 
 
+# Seeds chosen so that, on a 256-CU device, the launches cover the large-grid
+# paired (49, 1), 4-wave plain (5, 32), 8-wave paired (114, 159, 338) and
+# 8-wave plain (13, 3) forms, with both head dims and accumulate on and off.
+@pytest.mark.parametrize("seed", [49, 1, 5, 32, 114, 159, 338, 13, 3])
+def test_jobs_random_diagonal_steps(ra, seed):
+    """Seeded random head-tail diagonal steps (two jobs, the tail job over two
+    segments): part lengths 64..2400, 16..64 query heads, MHA or GQA, d 64
+    or 128, fresh or accumulating.  Small and large grids, paired and not,
+    as the host's cost model decides; sampled heads against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    c = int(rng.integers(64, 2401))
+    d = int(rng.choice([64, 128]))
+    hq = int(rng.choice([16, 32, 64]))
+    hkv = int(rng.choice([hq, 8]))
+    accumulate = bool(rng.integers(0, 2))
+    pre = int(rng.integers(1, 130))
+    gap = int(rng.integers(1, 8))            # the tail part sits gap parts after the head
+    say(f"seed {seed}: c={c} d={d} hq={hq} hkv={hkv} acc={accumulate} pre={pre} gap={gap}")
+    cfg = 300 + seed
+    q, _ = tensor(cfg, 1, 0, (1, 2 * c, hq, d), torch.bfloat16)
+    k, _ = tensor(cfg, 2, 0, (1, 2 * c, hkv, d), torch.bfloat16)
+    v, _ = tensor(cfg, 3, 0, (1, 2 * c, hkv, d), torch.bfloat16)
+    k_pre, _ = tensor(cfg, 4, 0, (1, pre, hkv, d), torch.bfloat16)
+    v_pre, _ = tensor(cfg, 5, 0, (1, pre, hkv, d), torch.bfloat16)
+    o = torch.empty((1, 2 * c, hq, d), device="cuda")
+    lse = torch.empty((1, 2 * c, hq), device="cuda")
+    head0, tail0 = pre, pre + gap * c
+    k_head, v_head = k[:, :c].contiguous(), v[:, :c].contiguous()
+    k_tail, v_tail = k[:, c:].contiguous(), v[:, c:].contiguous()
+    if accumulate:
+        for part, q0 in ((slice(0, c), head0), (slice(c, 2 * c), tail0)):
+            ra.ring_attn_step(q[:, part], k_pre, v_pre, o[:, part], lse[:, part], q_pos0=q0,
+                              k_pos0=0, causal=True)
+    jobs = [dict(q=q[:, :c], o=o[:, :c], lse=lse[:, :c], q_pos0=head0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0)]),
+            dict(q=q[:, c:], o=o[:, c:], lse=lse[:, c:], q_pos0=tail0, accumulate=accumulate,
+                 segments=[(k_head, v_head, head0), (k_tail, v_tail, tail0)])]
+    ra.ring_attn_step_jobs(jobs, causal=True)
+    torch.cuda.synchronize()
+    group = hq // hkv
+    heads = sorted({0, int(rng.integers(0, hq)), hq - 1})
+    kv_heads = [h // group for h in heads]
+    q64 = host64(q)[:, :, heads]
+    k64, v64 = host64(k)[:, :, kv_heads], host64(v)[:, :, kv_heads]
+    pos = np.concatenate([head0 + np.arange(c), tail0 + np.arange(c)])
+    kpos = pos
+    if accumulate:
+        k64 = np.concatenate([host64(k_pre)[:, :, kv_heads], k64], 1)
+        v64 = np.concatenate([host64(v_pre)[:, :, kv_heads], v64], 1)
+        kpos = np.concatenate([np.arange(pre), pos])
+    ro, rl = oracle.attention_ref(q64, k64, v64, pos, kpos, True)
+    compare(host64(o)[:, :, heads], host64(lse)[:, :, heads], ro, rl, BF16_O, BF16_LSE,
+            f"random diagonal step {seed}")
+
+
 def _decode_paged_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs, il, spare_blocks,
                        drop=None):
     """Paged caches: each request has its own block table (a random choice of
