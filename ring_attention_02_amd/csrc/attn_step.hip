@@ -18,9 +18,11 @@
 //  * workgroup = 4 waves = 128 query rows of one (job, batch, query head);
 //    each wave owns 32 rows whose Q fragment stays in registers for the
 //    sweep; grids under two workgroups per CU use 8 waves (two key-split
-//    halves merged through LDS), grids with at least two 256-row
-//    workgroups per CU use 8 waves on 256 rows sharing every K/V tile, and a
-//    complementary two-job step can pair two query tiles in one workgroup;
+//    halves that swap half their output blocks through LDS, then each
+//    finalise and store half of the d_v columns), grids with at least two
+//    256-row workgroups per CU use 8 waves on 256 rows sharing every K/V
+//    tile, and a complementary two-job step can pair two query tiles in one
+//    workgroup (on small and large grids);
 //  * K/V tiles of 64 keys go HBM -> LDS with bounded buffer loads (one
 //    descriptor per segment, the tile offset in soffset; rows past a segment
 //    read as zero), two stages each, XOR-swizzled 16-byte chunks for
@@ -32,7 +34,8 @@
 //    contraction order over keys is permuted to match the score layout, and
 //    V^T is read with ds_read_b64_tr_b16 from row-major V in LDS;
 //  * the next tile's S^T MFMAs are interleaved with this tile's
-//    exponentials, then P V runs with its LDS reads kept ahead of the MFMAs;
+//    exponentials at raised wave priority, then P V runs with its LDS reads
+//    kept ahead of the MFMAs;
 //  * exp2-domain online softmax with a lazily raised running max; tiles that
 //    need no mask skip it with one compare.
 #include <hip/hip_runtime.h>
