@@ -444,7 +444,9 @@ def cpu_baseline(w):
     from seeded_inputs import CONFIGS, Q_ID, K_ID, V_ID
     c1 = CONFIGS[1]
     shape1 = (c1["batch"], c1["seq"], c1["heads"], c1["d"])
-    q1, k1, v1 = (workloads.host_tensor(1, t, 0, shape1, torch_f32()).cpu().numpy() for t in (Q_ID, K_ID, V_ID))
+    import torch
+    q1, k1, v1 = (workloads.host_tensor(1, t, 0, shape1, torch.float32).cpu().numpy()
+                  for t in (Q_ID, K_ID, V_ID))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         oracle.attention_ref(q[None, :, :1], k[None, :, :1], v[None, :, :1], q_pos,
@@ -462,10 +464,6 @@ def cpu_baseline(w):
                                     "seconds": round(t_c1, 4)}}
     return out
 
-
-def torch_f32():
-    import torch
-    return torch.float32
 
 
 def main():
