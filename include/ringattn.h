@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define RINGATTN_ABI_VERSION 2
+#define RINGATTN_ABI_VERSION 3
 
 typedef enum {
   CP_OK = 0,
@@ -130,15 +130,35 @@ int32_t cp_slot_mapping(const int64_t* positions, int64_t n, int32_t block_size,
  * tokens in original order), src_idx gets the gathered row of that token.
  *
  *   seq_lens  host int64 [num_reqs] context lengths.
- *   src_idx   host int64 [sum seq_lens], or NULL to query the length.
- *   src_len   host int64 out: sum of seq_lens (may be NULL).
- *   dev_lens  host int64 [W * num_reqs] out, device-major: tokens of request
- *             r on device d (may be NULL).
- * CP_EINVAL as cp_slot_mapping for the sizes; negative lengths are invalid.
+ *   src_idx   host int64 [*src_len] out, or NULL to query the length.
+ *   src_len   host int64 in: capacity of src_idx (required when src_idx is
+ *             not NULL); out: sum of seq_lens.  May be NULL when src_idx is.
+ *   dev_lens  host int64 [dev_lens_len] out, device-major: dev_lens[d *
+ *             num_reqs + r] = tokens of request r on device d (may be NULL).
+ *   dev_lens_len  capacity of dev_lens (at least W * num_reqs when given).
+ * CP_EINVAL as cp_slot_mapping for the sizes; negative lengths and a
+ * capacity smaller than needed are CP_EINVAL (nothing is written).
  * ---------------------------------------------------------------------- */
 int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int32_t block_size,
                        int32_t interleave, int32_t pcp_size, int32_t dcp_size, int64_t* src_idx,
-                       int64_t* src_len, int64_t* dev_lens);
+                       int64_t* src_len, int64_t* dev_lens, int64_t dev_lens_len);
+
+/* ------------------------------------------------------------------------
+ * cp_ring_schedule -- which K/V block a rank computes with at each ring step.
+ * [RA] ring-topology excerpt: at step t device i holds the block that
+ * started on device (i - t) mod N, received from device i - 1 while it
+ * passes its previous block on to device i + 1; after N steps every device
+ * has met every block once.  [CP] head-tail partition: the block of rank s
+ * carries sequence parts s and 2N-1-s (of 2N).
+ *
+ *   rank, cp_size  0 <= rank < cp_size.
+ *   src_rank  host int32 [cp_size] out, or NULL: src_rank[t] = rank whose
+ *             block `rank` computes with at step t (step 0 is its own).
+ *   parts     host int32 [2 * cp_size] out, or NULL: parts[2t], parts[2t+1]
+ *             = the head and tail part of that block.
+ * At least one output must be given (CP_EINVAL otherwise).
+ * ---------------------------------------------------------------------- */
+int32_t cp_ring_schedule(int32_t rank, int32_t cp_size, int32_t* src_rank, int32_t* parts);
 
 /* ------------------------------------------------------------------------
  * cp_classify -- class of one (Q range, KV range) block pair.
@@ -211,8 +231,9 @@ int32_t ring_attn_step(const void* q, const void* k, const void* v, int32_t dtyp
  * stream, event or copy kernel is needed.  dst / src are device pointers,
  * 16-byte aligned, bytes a multiple of 16.  A dst range may overlap no
  * other forward range (src or dst) and no q / o / lse / k / v buffer of the
- * jobs (CP_EINVAL).  The copies complete with the launch (stream order),
- * also when no job has any visible key.
+ * jobs, and a src range no o / lse buffer of the jobs (CP_EINVAL).  The
+ * copies complete with the launch (stream order), also when no job has any
+ * visible key.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const void* k;   /* [batch, sk, hkv, d_qk] */

@@ -21,14 +21,14 @@ CP_OK, CP_EINVAL, CP_EDTYPE, CP_EUNSUPPORTED, CP_EHIP = 0, 1, 2, 3, 4
 CP_BF16, CP_F32 = 0, 1
 CP_MASK_NONE, CP_MASK_CAUSAL = 0, 1
 FULL, DIAG, SKIP = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/ringattn.h declares.
 EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition",
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
             "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
             "ring_attn_step_jobs", "split_kv_decode_paged", "ring_attn_step_varlen",
-            "cp_gather_rows", "cp_reorg_index")
+            "cp_gather_rows", "cp_reorg_index", "cp_ring_schedule")
 
 
 class RingAttnError(RuntimeError):
@@ -56,7 +56,9 @@ _lib.cp_slot_mapping.restype = _i32
 _lib.cp_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp]
 _lib.cp_classify.restype = _i32
 _lib.cp_reorg_index.restype = _i32
-_lib.cp_reorg_index.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _pi64, _vp]
+_lib.cp_reorg_index.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _pi64, _vp, _i64]
+_lib.cp_ring_schedule.restype = _i32
+_lib.cp_ring_schedule.argtypes = [_i32, _i32, _vp, _vp]
 _lib.cp_classify.argtypes = [_i64, _i64, _i64, _i64, _i32, _pi32]
 _lib.ring_attn_step.restype = _i32
 _lib.ring_attn_step.argtypes = [_vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
@@ -160,12 +162,23 @@ def reorg_index(seq_lens, block_size, interleave, pcp_size, dcp_size):
     W = pcp_size * dcp_size
     dev_lens = np.zeros((W, lens.size), dtype=np.int64)
     _check(_lib.cp_reorg_index(_np_ptr(lens), lens.size, block_size, interleave, pcp_size, dcp_size,
-                               None, ctypes.byref(n), _np_ptr(dev_lens)), "cp_reorg_index")
+                               None, ctypes.byref(n), _np_ptr(dev_lens), dev_lens.size),
+           "cp_reorg_index")
     src = np.empty(n.value, dtype=np.int64)
     if n.value:
         _check(_lib.cp_reorg_index(_np_ptr(lens), lens.size, block_size, interleave, pcp_size,
-                                   dcp_size, _np_ptr(src), ctypes.byref(n), None), "cp_reorg_index")
+                                   dcp_size, _np_ptr(src), ctypes.byref(n), None, 0), "cp_reorg_index")
     return src, dev_lens
+
+
+def ring_schedule(cp_size, rank):
+    """Ring order of `rank`: (src_rank int32[cp], parts int32[cp, 2]) -- the rank
+    whose K/V block it computes with at each step, and that block's head and
+    tail sequence parts under the head-tail partition."""
+    src = np.empty(cp_size, dtype=np.int32)
+    parts = np.empty((cp_size, 2), dtype=np.int32)
+    _check(_lib.cp_ring_schedule(rank, cp_size, _np_ptr(src), _np_ptr(parts)), "cp_ring_schedule")
+    return src, parts
 
 
 def classify(q_pos0, sq, k_pos0, sk, causal=True):
@@ -468,7 +481,7 @@ def stage_copy(pairs, stream=None):
 
 from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E402
 
-__all__ = ["partition", "slot_mapping", "reorg_index", "classify", "ring_attn_step", "ring_attn_step_jobs",
+__all__ = ["partition", "slot_mapping", "reorg_index", "ring_schedule", "classify", "ring_attn_step", "ring_attn_step_jobs",
            "lse_merge", "stage_copy",
            "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged",
            "ring_attn_step_varlen", "gather_rows", "ZigzagRing", "segmented_prefill",

@@ -461,8 +461,12 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   // ends at the segment's last key of this (batch, kv head), and the tile
   // offset goes in the uniform soffset.  Rows past the end of the segment
   // read as zeros (their scores are masked), so no tile needs a tail path.
-  // The descriptor is rebuilt only when the sweep enters a segment or has
-  // moved 2^30 bytes past its base.  Wave-instruction i fills 64 consecutive
+  // The range check of a raw buffer load covers the per-lane offset only,
+  // not the uniform soffset, so the segment's partial last tile is always
+  // loaded from a descriptor based at that tile (soffset 0): its rows past
+  // the end are then outside the record count.  The descriptor is rebuilt
+  // only when the sweep enters a segment, reaches that tile or has moved
+  // 2^30 bytes past its base.  Wave-instruction i fills 64 consecutive
   // 16-byte LDS slots; each lane fetches the logical chunk the swizzle maps
   // to its slot, at a loop-invariant byte offset inside the tile.
   const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
@@ -486,18 +490,22 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   const int tile_bytes_v = static_cast<int>(kBN * row_elems_v * 2);
   const int rebase_k = (1 << 30) / tile_bytes_k, rebase_v = (1 << 30) / tile_bytes_v;
   struct DmaCursor {
-    int sg, start, end, base_vt;
+    int sg, start, end, base_vt, tail_vt;
     __amdgpu_buffer_rsrc_t rsrc;
   };
+  constexpr int kNoTail = 0x7FFFFFFF;
   auto seek = [&](DmaCursor& c, int vt, bool is_k) {
     advance(c.sg, c.start, c.end, vt);
     const int64_t sk = seg_sk(c.sg);
     const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
     const int width = is_k ? DQK : DV;
     const uint16_t* base = seg_base(c.sg, is_k) + (static_cast<int64_t>(b) * sk * a.hkv + kvh) * width;
-    // a backward sweep bases the descriptor below vt so the next tiles reuse it
+    // the segment's partial last tile (rows past sk), if the sweep reaches it
+    c.tail_vt = sk % kBN != 0 ? c.start + static_cast<int>(sk / kBN) : kNoTail;
+    // a backward sweep bases the descriptor below vt so the next tiles reuse
+    // it; the partial last tile is based at itself
     const int rebase = is_k ? rebase_k : rebase_v;
-    const int base_vt = rev ? max(c.start, vt - rebase + 1) : vt;
+    const int base_vt = rev && vt != c.tail_vt ? max(c.start, vt - rebase + 1) : vt;
     const int64_t key0 = static_cast<int64_t>(base_vt - c.start) * kBN;
     // bytes from the base tile to the end of key sk-1's row of this head
     const int64_t valid = ((sk - 1 - key0) * row_elems + width) * 2;
@@ -507,9 +515,11 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
                                                static_cast<short>(0), nrec, 0x00020000);
   };
   const auto no_rsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(nullptr), static_cast<short>(0), 0, 0);
-  DmaCursor kcur{-1, 0, 0, 0, no_rsrc}, vcur{-1, 0, 0, 0, no_rsrc};
+  DmaCursor kcur{-1, 0, 0, 0, kNoTail, no_rsrc}, vcur{-1, 0, 0, 0, kNoTail, no_rsrc};
   auto dma_k = [&](int vt, int stage) {
-    if (vt >= kcur.end || vt < kcur.base_vt || vt - kcur.base_vt >= rebase_k) seek(kcur, vt, true);
+    if (vt >= kcur.end || vt < kcur.base_vt || vt - kcur.base_vt >= rebase_k ||
+        (vt == kcur.tail_vt && vt != kcur.base_vt))
+      seek(kcur, vt, true);
     const int soff = (vt - kcur.base_vt) * tile_bytes_k;
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
@@ -519,7 +529,9 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
           static_cast<int>(koffb[i]), soff, 0, 0);
   };
   auto dma_v = [&](int vt, int stage) {
-    if (vt >= vcur.end || vt < vcur.base_vt || vt - vcur.base_vt >= rebase_v) seek(vcur, vt, false);
+    if (vt >= vcur.end || vt < vcur.base_vt || vt - vcur.base_vt >= rebase_v ||
+        (vt == vcur.tail_vt && vt != vcur.base_vt))
+      seek(vcur, vt, false);
     const int soff = (vt - vcur.base_vt) * tile_bytes_v;
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
@@ -1265,8 +1277,8 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
                    !overlaps(jobs[i].lse, lse_bytes, jb.lse, lse_bytes),
                CP_EINVAL, "ring_attn_step_jobs: jobs %d and %d write overlapping outputs", i, j);
   }
-  // Forwarded ranges: aligned, and every destination disjoint from all else
-  // the launch reads or writes.
+  // Forwarded ranges: aligned, every destination disjoint from all else the
+  // launch reads or writes, and every source disjoint from what it writes.
   RA_CHECK(n_forward >= 0 && n_forward <= kMaxFwd && (n_forward == 0 || forward != nullptr),
            CP_EINVAL, "ring_attn_step_jobs: n_forward=%d outside [0, %d]", n_forward, kMaxFwd);
   for (int f = 0; f < n_forward; ++f) {
@@ -1285,8 +1297,11 @@ extern "C" int32_t ring_attn_step_jobs(const cp_attn_job_t* jobs, int32_t n_jobs
     if (rows == 0) continue;
     for (int j = 0; j < n_jobs; ++j) {
       const cp_attn_job_t& jb = jobs[j];
+      // (a source may not be an output either: the outputs are written
+      // while the slices are copied)
       bool hit = overlaps(c.dst, c.bytes, jb.q, rows * d_qk * 2) ||
-                 overlaps(c.dst, c.bytes, jb.o, o_bytes) || overlaps(c.dst, c.bytes, jb.lse, lse_bytes);
+                 overlaps(c.dst, c.bytes, jb.o, o_bytes) || overlaps(c.dst, c.bytes, jb.lse, lse_bytes) ||
+                 overlaps(c.src, c.bytes, jb.o, o_bytes) || overlaps(c.src, c.bytes, jb.lse, lse_bytes);
       for (int sg = 0; sg < jb.n_segments; ++sg) {
         const cp_kv_segment_t& sgm = jb.segments[sg];
         const int64_t kv_rows = static_cast<int64_t>(batch) * sgm.sk * hkv;

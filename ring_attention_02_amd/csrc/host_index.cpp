@@ -143,7 +143,8 @@ extern "C" int32_t cp_slot_mapping(const int64_t* positions, int64_t n, int32_t 
 // gathered buffer; the device gather (cp_gather_rows) then moves the rows.
 extern "C" int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int32_t block_size,
                                   int32_t interleave, int32_t pcp_size, int32_t dcp_size,
-                                  int64_t* src_idx, int64_t* src_len, int64_t* dev_lens) {
+                                  int64_t* src_idx, int64_t* src_len, int64_t* dev_lens,
+                                  int64_t dev_lens_len) {
   RA_CHECK(num_reqs >= 0, CP_EINVAL, "cp_reorg_index: num_reqs=%d < 0", num_reqs);
   RA_CHECK(num_reqs == 0 || seq_lens, CP_EINVAL, "cp_reorg_index: NULL seq_lens");
   RA_CHECK(block_size > 0 && interleave > 0 && pcp_size > 0 && dcp_size > 0, CP_EINVAL,
@@ -151,14 +152,26 @@ extern "C" int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int
            block_size, interleave, pcp_size, dcp_size);
   RA_CHECK(block_size % interleave == 0, CP_EINVAL,
            "cp_reorg_index: block_size %d is not a multiple of interleave %d", block_size, interleave);
+  RA_CHECK(src_idx == nullptr || src_len != nullptr, CP_EINVAL,
+           "cp_reorg_index: src_len (the capacity of src_idx) must not be NULL");
   int64_t total = 0;
   for (int32_t r = 0; r < num_reqs; ++r) {
     RA_CHECK(seq_lens[r] >= 0, CP_EINVAL, "cp_reorg_index: seq_lens[%d] < 0", r);
+    RA_CHECK(seq_lens[r] <= std::numeric_limits<int64_t>::max() / 4 - total, CP_EINVAL,
+             "cp_reorg_index: total length overflows");
     total += seq_lens[r];
   }
-  if (src_len) *src_len = total;
   const int64_t world = static_cast<int64_t>(pcp_size) * dcp_size;
   const int64_t vbs = static_cast<int64_t>(block_size) * world;
+  // capacities are checked before anything is written
+  if (src_idx != nullptr)
+    RA_CHECK(*src_len >= total, CP_EINVAL, "cp_reorg_index: src_idx capacity %lld < needed %lld",
+             static_cast<long long>(*src_len), static_cast<long long>(total));
+  if (dev_lens != nullptr)
+    RA_CHECK(dev_lens_len >= world * num_reqs, CP_EINVAL,
+             "cp_reorg_index: dev_lens capacity %lld < needed %lld", static_cast<long long>(dev_lens_len),
+             static_cast<long long>(world * num_reqs));
+  if (src_len) *src_len = total;
   // tokens of request r on device d
   std::vector<int64_t> len(static_cast<size_t>(world * num_reqs), 0);
   for (int32_t r = 0; r < num_reqs; ++r)
@@ -181,6 +194,32 @@ extern "C" int32_t cp_reorg_index(const int64_t* seq_lens, int32_t num_reqs, int
       const int64_t slot = (x / vbs) * block_size + (lbi / world) * interleave + off % interleave;
       src_idx[out++] = base[dev * num_reqs + r] + slot;
     }
+  return ok();
+}
+
+// Ring order: guijiagi.com "Ring Attention", ring-topology excerpt -- at
+// step t device i computes with the K/V block that started on device
+// (i - t) mod N, received from its predecessor, and passes it on to its
+// successor; after N steps it has met every block once.  With the head-tail
+// partition (vLLM-Ascend "Context Parallel (CP)", PCP head-tail token
+// partition paragraph) the block of rank s carries parts s and 2N-1-s.
+extern "C" int32_t cp_ring_schedule(int32_t rank, int32_t cp_size, int32_t* src_rank,
+                                    int32_t* parts) {
+  RA_CHECK(cp_size > 0, CP_EINVAL, "cp_ring_schedule: cp_size=%d must be > 0", cp_size);
+  RA_CHECK(rank >= 0 && rank < cp_size, CP_EINVAL, "cp_ring_schedule: rank=%d outside [0,%d)", rank,
+           cp_size);
+  RA_CHECK(src_rank != nullptr || parts != nullptr, CP_EINVAL,
+           "cp_ring_schedule: src_rank and parts are both NULL");
+  for (int32_t t = 0; t < cp_size; ++t) {
+    // the block moves one rank per step, so after t steps rank `rank` holds
+    // the one that started t ranks before it (mod N)
+    const int32_t s = static_cast<int32_t>((static_cast<int64_t>(rank) - t + cp_size) % cp_size);
+    if (src_rank) src_rank[t] = s;
+    if (parts) {
+      parts[2 * t] = s;
+      parts[2 * t + 1] = 2 * cp_size - 1 - s;
+    }
+  }
   return ok();
 }
 

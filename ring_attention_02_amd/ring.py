@@ -23,7 +23,8 @@ rank's own block in place.
 
 import math
 
-from . import ring_attn_step, ring_attn_step_jobs, lse_merge, classify, stage_copy, FULL, DIAG, SKIP
+from . import (ring_attn_step, ring_attn_step_jobs, lse_merge, classify, stage_copy, ring_schedule,
+               FULL, DIAG, SKIP)
 
 
 def _torch():
@@ -47,9 +48,10 @@ class ZigzagRing:
         self.cp, self.rank = cp_size, rank
         self.chunk = seq // (2 * cp_size)
         c = self.chunk
-        self.q_parts = (rank, 2 * cp_size - 1 - rank)
-        self.steps = [((rank - t) % cp_size, 2 * cp_size - 1 - (rank - t) % cp_size)
-                      for t in range(cp_size)]
+        # the block's (head, tail) parts at each step, from the library's ring
+        # order; step 0 is the rank's own block, whose parts are its queries
+        self.steps = [tuple(int(p) for p in pair) for pair in ring_schedule(cp_size, rank)[1]]
+        self.q_parts = self.steps[0]
         dev = k_full.device
         self.kbuf = [torch.empty((2, 1, c, *k_full.shape[2:]), dtype=k_full.dtype, device=dev)
                      for _ in range(2)]
@@ -85,7 +87,9 @@ class ZigzagRing:
         copy_stream (a torch stream) the copies run on it instead, in
         ring_stage_copy launches ordered against the steps by events.
         on_launch(step, q_index, kv_index, cls, fn) may wrap each launch (the
-        bench uses it to time launches); fn() performs the launch.
+        bench uses it to time launches); fn() performs the launch, and
+        fn.jobs / fn.forward are the jobs and forwarded (dst, src) pairs it
+        passes to ring_attn_step_jobs.
         """
         c = self.chunk
         first = [True, True]
@@ -136,6 +140,7 @@ class ZigzagRing:
             if jobs:
                 def fn(j=jobs, f=fwd):
                     ring_attn_step_jobs(j, causal=True, scale=scale, forward=f)
+                fn.jobs, fn.forward = jobs, fwd
                 if on_launch is None:
                     fn()
                 else:
@@ -226,8 +231,9 @@ def noncausal_ring_sweep(q, k, v, n_blocks, scale=None):
     lse_parts = torch.empty((n_blocks, B, S, H), dtype=torch.float32, device=q.device)
     for qb in range(n_blocks):
         qs = slice(qb * blk, (qb + 1) * blk)
+        order = ring_schedule(n_blocks, qb)[0]        # block of each ring step
         for t in range(n_blocks):
-            kb = (qb - t) % n_blocks
+            kb = int(order[t])
             ks = slice(kb * blk, (kb + 1) * blk)
             ring_attn_step(q[:, qs], k[:, ks].contiguous(), v[:, ks].contiguous(),
                            o_parts[t][:, qs], lse_parts[t][:, qs], q_pos0=qb * blk,

@@ -28,11 +28,11 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(ra):
     declared = _declared_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 17, declared
     assert sorted(ra.EXPORTED) == declared
     for name in declared:
         assert hasattr(ra.lib(), name), name
-    assert ra.lib().cp_abi_version() == 2
+    assert ra.lib().cp_abi_version() == 3
     assert ra.lib().cp_status_string(1).decode().startswith("CP_EINVAL")
 
 
@@ -78,6 +78,26 @@ def test_classify_matches_oracle(ra):
                     for causal in (False, True):
                         assert ra.classify(q0, sq, k0, sk, causal) == \
                             oracle.classify_ref(q0, sq, k0, sk, causal)
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8, 16])
+def test_ring_schedule_bit_exact(ra, cp):
+    for rank in range(cp):
+        src, parts = ra.ring_schedule(cp, rank)
+        assert src.tolist() == oracle.ring_schedule_ref(rank, cp)
+        assert [tuple(p) for p in parts.tolist()] == oracle.zigzag_ring_chunks_ref(rank, cp)
+
+
+def test_ring_schedule_errors(ra):
+    lib = ra.lib()
+    src = np.full(4, -7, dtype=np.int32)
+    assert lib.cp_ring_schedule(4, 4, src.ctypes.data, None) == ra.CP_EINVAL
+    assert lib.cp_ring_schedule(-1, 4, src.ctypes.data, None) == ra.CP_EINVAL
+    assert lib.cp_ring_schedule(0, 0, src.ctypes.data, None) == ra.CP_EINVAL
+    assert lib.cp_ring_schedule(0, 4, None, None) == ra.CP_EINVAL
+    assert np.all(src == -7)
+    assert lib.cp_ring_schedule(1, 4, src.ctypes.data, None) == ra.CP_OK
+    assert src.tolist() == [1, 0, 3, 2]
 
 
 def _status(fn, *args):
@@ -218,6 +238,9 @@ def test_jobs_validate_before_launch(ra):
     assert call([a], fwd=[cp(4096, 32 << 20, 64)]) == ra.CP_EINVAL            # onto segment k
     assert call([a], fwd=[cp(free, 32 << 20, 4096), cp(free + 2048, 48 << 20, 4096)]) == ra.CP_EINVAL
     assert call([a], fwd=[cp(free, free + 1024, 4096)]) == ra.CP_EINVAL       # dst overlaps own src
+    # a source inside an output the launch writes (o, then lse)
+    assert call([a], fwd=[cp(free, (2 << 20) + 64, 4096)]) == ra.CP_EINVAL and "job 0" in ra.last_error()
+    assert call([a], fwd=[cp(free, 3 << 20, 64)]) == ra.CP_EINVAL and "job 0" in ra.last_error()
 
 
 def test_decode_paged_validates_before_launch(ra):
@@ -285,8 +308,27 @@ def test_reorg_index_errors(ra):
     lens = np.array([10, -1], dtype=np.int64)
     n = ctypes.c_int64(0)
     assert lib.cp_reorg_index(ctypes.c_void_p(lens.ctypes.data), 2, 4, 2, 2, 1, None, ctypes.byref(n),
-                              None) == ra.CP_EINVAL
+                              None, 0) == ra.CP_EINVAL
     ok = np.array([10], dtype=np.int64)
     assert lib.cp_reorg_index(ctypes.c_void_p(ok.ctypes.data), 1, 6, 4, 2, 1, None, ctypes.byref(n),
-                              None) == ra.CP_EINVAL and "multiple" in ra.last_error()
-    assert lib.cp_reorg_index(None, 1, 4, 2, 2, 1, None, ctypes.byref(n), None) == ra.CP_EINVAL
+                              None, 0) == ra.CP_EINVAL and "multiple" in ra.last_error()
+    assert lib.cp_reorg_index(None, 1, 4, 2, 2, 1, None, ctypes.byref(n), None, 0) == ra.CP_EINVAL
+    # capacities: a short src_idx or dev_lens is rejected before anything is written
+    two = np.array([10, 7], dtype=np.int64)
+    src = np.full(17, -7, dtype=np.int64)
+    dev = np.full(4, -7, dtype=np.int64)
+    n.value = 16
+    assert lib.cp_reorg_index(ctypes.c_void_p(two.ctypes.data), 2, 4, 2, 2, 1, ctypes.c_void_p(src.ctypes.data),
+                              ctypes.byref(n), ctypes.c_void_p(dev.ctypes.data), 4) == ra.CP_EINVAL
+    assert "capacity" in ra.last_error() and n.value == 16
+    n.value = 17
+    assert lib.cp_reorg_index(ctypes.c_void_p(two.ctypes.data), 2, 4, 2, 2, 1, ctypes.c_void_p(src.ctypes.data),
+                              ctypes.byref(n), ctypes.c_void_p(dev.ctypes.data), 3) == ra.CP_EINVAL
+    assert "dev_lens" in ra.last_error()
+    assert np.all(src == -7) and np.all(dev == -7)
+    assert lib.cp_reorg_index(ctypes.c_void_p(two.ctypes.data), 2, 4, 2, 2, 1, ctypes.c_void_p(src.ctypes.data),
+                              None, None, 0) == ra.CP_EINVAL                  # no capacity given
+    assert lib.cp_reorg_index(ctypes.c_void_p(two.ctypes.data), 2, 4, 2, 2, 1, ctypes.c_void_p(src.ctypes.data),
+                              ctypes.byref(n), ctypes.c_void_p(dev.ctypes.data), 4) == ra.CP_OK
+    ref_src, ref_lens = oracle.reorg_index_ref([10, 7], 4, 2, 2, 1)
+    assert np.array_equal(src, ref_src) and np.array_equal(dev.reshape(2, 2), ref_lens)
