@@ -3,29 +3,30 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--primary-only]
                     [--no-cpu-baseline]
 
-Prints ONE JSON line.  The headline workload is the zigzag causal ring
-prefill of one rank: seq 8192, cp 4 (8 chunks of 1024), rank 0 holding Q
-chunks {0, 7}, 32 heads, d 128, bf16 with float32 accumulation.  A step is
-one full ring sweep of that rank: 4 ring steps of one launch each, which
-computes the (Q chunk, K/V chunk) pairs of the current block (7 FULL, 2 DIAG
-and 7 SKIP pairs overall, merged in place) and copies the next K/V block
-into the idle staging slot.
+Prints ONE JSON line.  The headline workload is the long zigzag causal ring
+prefill of one rank: a 1,048,576-token sequence at cp 8 (16 chunks of
+65,536), rank 0 holding Q chunks {0, 15} (131,072 local queries), 64 query
+heads over 8 kv heads, d 128, bf16 with float32 accumulation.  A step is one
+full ring sweep of that rank: 8 ring steps of one launch each, which compute
+the (Q chunk, K/V chunk) pairs of the block the rank holds (15 FULL, 2 DIAG
+and 15 SKIP pairs overall, merged in place) and copy the next K/V block
+into the idle staging slot.  W untimed sweeps, then exactly K timed sweeps
+between two device synchronisations.
 `value` is algorithmic causal-attention TFLOP/s: visible (q, k) pairs x
-heads x (2 d_qk + 2 d_v) per sweep / time per sweep.  The K timed sweeps
-are captured as one HIP graph (each sweep recomputes everything from the
-same inputs) and replayed once between two synchronisations, after W
-untimed sweeps.  Reported beside it under "launch": one graph per sweep
-replayed K times, plain eager issue, and the same sweep with the staging
-copies on a side stream (ring_stage_copy launches ordered by events).
+heads x (2 d_qk + 2 d_v) per sweep / time per sweep.  The roofline entry
+averages the ring-step kernel's launches of the timed sweeps, each timed
+with HIP events on the stream it is launched on.
 
-Also reported in the same line (unless --primary-only): the long zigzag
-prefill (rank 0 of cp=8 over 1M tokens), GQA decode over 8 sequence shards
-(GB/s against HBM), the same decode over paged caches read through block
-tables, segmented chunked prefill (MLA shape), a packed multi-request
-(varlen) prefill, the all-gather-KV reorganisation gather, the tiny fp32
-non-causal ring (a correctness workload, timed for completeness) and a
-standalone LSE merge, each with the roofline of its dominant kernel, plus
-the CPU oracle timed on the host (all its threads, and on one thread).
+Also reported in the same line (unless --primary-only): the short zigzag
+prefill (rank 0 of cp 4 over 8192 tokens, with its copy/compute overlap),
+GQA decode over 8 sequence shards (GB/s against HBM), the same decode over
+paged caches read through block tables, segmented chunked prefill (MLA
+shape), a packed multi-request (varlen) prefill, the all-gather-KV
+reorganisation gather, the tiny fp32 non-causal ring (a correctness
+workload, timed for completeness) and a standalone LSE merge, each with the
+roofline of its dominant kernel; and the CPU oracle timed on the host on a
+bounded sample of the headline workload (extrapolated by visible pairs),
+with the same for the other workloads beside it.
 """
 
 import argparse
@@ -45,8 +46,8 @@ METRIC = "causal attn TFLOP/s per ring-step prefill + decode GB/s, % of roofline
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--primary-only", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of secondary workloads to run")
@@ -60,6 +61,8 @@ def parse():
                    help="only run the standalone LSE merge K times (for counter passes)")
     p.add_argument("--long-step-only", type=int, default=0, metavar="K",
                    help="only run one FULL ring-step launch of the 1M-token prefill K times")
+    p.add_argument("--long-sweep-only", type=int, default=0, metavar="K",
+                   help="only run K sweeps of the 1M-token prefill (for counter passes)")
     return p.parse_args()
 
 
@@ -222,44 +225,122 @@ def blas_threads():
 # workloads
 # ---------------------------------------------------------------------------
 
-def zigzag_bench(cfg_id, steps, warmup, use_graph=True):
+def graph_ms(fns, sweeps, reps=3):
+    """Milliseconds per call sequence: `sweeps` copies of the launch list fns
+    captured back to back as one HIP graph (uploaded before its first launch),
+    replayed `reps` times between two HIP events on the replay stream."""
+    import torch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for fn in fns:                  # warm: first launch outside the graph
+            fn()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(sweeps):
+                for fn in fns:
+                    fn()
+    torch.cuda.synchronize()
+    graph_upload(graph)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        s.record()
+        for _ in range(reps):
+            graph.replay()
+        e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (reps * sweeps)
+
+
+def long_headline(steps, warmup):
+    """The 1M-token zigzag sweep of rank 0: W untimed sweeps, then exactly K
+    timed sweeps (one launch per ring step, issued from the host; at ~0.25 s
+    per launch issue cost is nil).  Every launch of the timed sweeps is
+    bracketed by HIP events on its own stream (the current stream, which the
+    binding launches on)."""
+    import torch
     import ring_attention_02_amd as ra
     import workloads
-    w = workloads.zigzag_setup(cfg_id)
+    w = workloads.zigzag_setup(4)
     ring, q, o, lse = w["ring"], w["q_local"], w["o"], w["lse"]
-    eager = time_steps(lambda: ring.run(q, o, lse), steps, warmup)
-    sec = eager
-    side_sec = per_graph_sec = None
-    if use_graph:
-        # one graph per sweep, replayed once per step
-        graph = ring.capture(q, o, lse)
-        per_graph_sec = time_steps(graph.replay, steps, warmup)
-        sec = per_graph_sec
-        if cfg_id == 2:
-            # the same sweep with the staging copies on a side stream
-            side_graph = ring.capture(q, o, lse, side_copies=True)
-            side_sec = time_steps(side_graph.replay, steps, warmup)
-            del side_graph
-            # the timed steps as one graph of `steps` sweeps: one graph launch
-            # for the whole job (each sweep still recomputes everything)
-            job = ring.capture(q, o, lse, sweeps=steps)
-            graph_upload(job)
-            for _ in range(warmup):
-                graph.replay()
-            sec = time_steps(job.replay, 1, 0) / steps
-            del job
-    launches = zigzag_launches(w)
-    reps = max(2, min(steps, 20)) if cfg_id == 2 else 1
-    mean_ms = kernel_launch_stats(launches, reps)
+    for _ in range(warmup):
+        ring.run(q, o, lse)
+    events = []
+
+    def timed(t, qi, kj, cls, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        events.append((cls, s, e))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ring.run(q, o, lse, on_launch=timed)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    durs = [(cls, s.elapsed_time(e)) for cls, s, e in events]
+    launches = len(durs) // steps
+    mean_ms = float(np.mean([d for _, d in durs]))
+    full_ms = float(np.mean([d for c, d in durs if c == ra.FULL]))
+    diag = [d for c, d in durs if c == ra.DIAG]
+    flops_per_launch = w["flops"] / launches
+    return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=launches,
+                        flops_per_launch=flops_per_launch,
+                        achieved_tflops=flops_per_launch / (mean_ms * 1e-3) / 1e12,
+                        full_ms=full_ms, diag_ms=float(np.mean(diag)) if diag else None)
+
+
+def short_zigzag_bench(sweeps=50, warmup=20):
+    """C2, the 8192-token sweep of rank 0 (cp 4): `sweeps` timed sweeps captured
+    as one HIP graph after `warmup` untimed ones (fixed counts, independent of
+    the headline's), plus other launch modes and the copy/compute overlap.
+
+    Overlap efficiency, (T_compute + T_copies - T_sweep) / T_copies: T_sweep
+    is the sweep as run (each step's launch also forwards the next block),
+    T_compute the same attention launches given no forwarded ranges, T_copies
+    the three block copies alone (ring_stage_copy launches); all three as
+    graphs of `sweeps` sequences."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.zigzag_setup(2)
+    ring, q, o, lse = w["ring"], w["q_local"], w["o"], w["lse"]
+    eager = time_steps(lambda: ring.run(q, o, lse), sweeps, warmup)
+    graph = ring.capture(q, o, lse)                   # one graph per sweep
+    per_graph = time_steps(graph.replay, sweeps, warmup)
+    side_graph = ring.capture(q, o, lse, side_copies=True)
+    side = time_steps(side_graph.replay, sweeps, warmup)
+    del side_graph
+    job = ring.capture(q, o, lse, sweeps=sweeps)      # the timed sweeps as one graph
+    graph_upload(job)
+    for _ in range(warmup):
+        graph.replay()
+    sec = time_steps(job.replay, 1, 0) / sweeps
+    del job
+    fns = []
+    ring.run(q, o, lse, on_launch=lambda t, qi, kj, cls, fn: fns.append((cls, fn)))
+    torch.cuda.synchronize()
+    launches = [fn for _, fn in fns]
+    reps = 20
+    mean_ms = graph_ms(launches, 1, reps) / len(launches)
+    full_ms = graph_ms([fn for c, fn in fns if c == ra.FULL], 1, reps) / sum(c == ra.FULL for c, _ in fns)
+    diag_ms = graph_ms([fn for c, fn in fns if c == ra.DIAG], 1, reps)
+    t_sweep = graph_ms(launches, sweeps)
+    compute = [lambda j=fn.jobs: ra.ring_attn_step_jobs(j, causal=True) for fn in launches]
+    t_compute = graph_ms(compute, sweeps)
+    copies = [lambda u=u: ra.stage_copy(ring.forward_pairs(u)) for u in range(1, ring.cp)]
+    t_copy = graph_ms(copies, sweeps)
     flops_per_launch = w["flops"] / len(launches)
-    achieved = flops_per_launch / (mean_ms * 1e-3) / 1e12
-    full_ms = kernel_launch_stats(zigzag_launches(w, ra.FULL), reps)
-    diag_ms = kernel_launch_stats(zigzag_launches(w, ra.DIAG), reps)
     return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=len(launches),
-                        flops_per_launch=flops_per_launch, achieved_tflops=achieved,
+                        achieved_tflops=flops_per_launch / (mean_ms * 1e-3) / 1e12,
                         full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3,
-                        side_ms=None if side_sec is None else side_sec * 1e3,
-                        per_graph_ms=None if per_graph_sec is None else per_graph_sec * 1e3)
+                        side_ms=side * 1e3, per_graph_ms=per_graph * 1e3,
+                        t_sweep_ms=t_sweep, t_compute_ms=t_compute, t_copy_ms=t_copy,
+                        overlap=(t_compute + t_copy - t_sweep) / t_copy)
 
 
 def tiny_bench(steps, warmup):
@@ -401,6 +482,21 @@ def long_step_only(reps):
     print(json.dumps({"long_step_launches": reps}), flush=True)
 
 
+def long_sweep_only(reps):
+    """K whole sweeps of the 1M-token zigzag prefill (rank 0, cp 8), nothing
+    else on the GPU after the input setup: for counter passes over the
+    headline's launches (8 per sweep: 7 FULL steps and the paired diagonal
+    step)."""
+    import torch
+    import workloads
+    w = workloads.zigzag_setup(4)
+    for _ in range(reps):
+        w["ring"].run(w["q_local"], w["o"], w["lse"])
+    torch.cuda.synchronize()
+    print(json.dumps({"long_sweeps": reps, "launches_per_sweep": 8, "flops_per_sweep": w["flops"]}),
+          flush=True)
+
+
 def merge_only(reps):
     """The standalone LSE merge alone, K launches, for counter passes."""
     import torch
@@ -413,38 +509,83 @@ def merge_only(reps):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle on the host, on a bounded sample of the workload
+# CPU baseline: the oracle on the host, on bounded samples of the workloads
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w):
+def host_cores():
+    """Host cores as the OS reports them, those this process may run on, and
+    the BLAS threads numpy's oracle actually uses."""
+    return {"os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads()}
+
+
+def _host64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def cpu_baseline_long(w):
+    """The oracle on 512 sampled (token, head) rows of the 1M-token rank-0
+    share, extrapolated to the whole sweep by visible-pair count.
+
+    Rows: 2 kv heads (the first and the last) x 4 of their query heads x 64
+    tokens, 32 of each local Q chunk at seeded random offsets.  Each batch of
+    32 rows goes to the oracle with the keys up to its last row's position,
+    causal by absolute position, so it computes (and masks) at least the
+    visible pairs it is credited with.  Only the oracle calls are timed."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(40404)
+    c, d, hq, hkv = w["chunk"], w["d"], w["hq"], w["hkv"]
+    group = hq // hkv
+    t_used, flops, rows = 0.0, 0, 0
+    for kvh in (0, hkv - 1):
+        k = _host64(w["k_full"][0, :, kvh])
+        v = _host64(w["v_full"][0, :, kvh])
+        for h in kvh * group + np.array([0, 3, 5, 7]) % group:
+            for i, part in enumerate(w["local_parts"]):
+                off = np.sort(rng.choice(c, 32, replace=False))
+                idx = torch.from_numpy(i * c + off).to(w["q_local"].device)
+                qr = _host64(w["q_local"][0, idx, int(h)])               # [32, d]
+                pos = part * c + off
+                n = int(pos.max()) + 1
+                t0 = time.perf_counter()
+                oracle.attention_ref(qr[None, :, None, :], k[None, :n, None, :], v[None, :n, None, :],
+                                     pos, np.arange(n), causal=True)
+                t_used += time.perf_counter() - t0
+                flops += int((pos + 1).sum()) * (2 * d + 2 * d)
+                rows += len(pos)
+        del k, v
+    rate = flops / t_used
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows} (token, head) rows of the 1M-token rank-0 share (2 kv heads x 4 query heads x "
+                      f"32 tokens of each local chunk), float64 numpy, {t_used:.1f} s; the rate is "
+                      f"extrapolated to the whole sweep by visible pairs",
+            "extrapolated": True, "extrapolated_seconds_per_sweep": round(w["flops"] / rate, 1),
+            **host_cores()}
+
+
+def cpu_baseline_short(w):
+    """The oracle on the whole 8192-token rank-0 share (every head, all its
+    threads), and on one thread for one head of it and for the whole tiny
+    fp32 ring workload."""
     import oracle
     import workloads
     k = w["k_full"][0].float().cpu().numpy().astype(np.float64)
     v = w["v_full"][0].float().cpu().numpy().astype(np.float64)
     q = w["q_local"][0].float().cpu().numpy().astype(np.float64)
     q_pos = np.asarray(w["local"], dtype=np.int64)
-    heads_done, pairs_done, t_used = 0, 0, 0.0
-    budget = 15.0
-    for h in range(w["hq"]):
-        t0 = time.perf_counter()
-        oracle.attention_ref(q[None, :, h:h + 1], k[None, :, h:h + 1], v[None, :, h:h + 1],
-                             q_pos, np.arange(k.shape[0]), causal=True)
-        t_used += time.perf_counter() - t0
-        heads_done += 1
-        if t_used > budget:
-            break
-    flops = w["pairs"] * heads_done * (2 * w["d"] + 2 * w["d"])
-    out = {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
-           "kind": "oracle",
-           "sample": f"rank-0 local queries (2048 tokens) x all 8192 keys for {heads_done} of "
-                     f"{w['hq']} heads, float64 numpy, {t_used:.1f} s"}
-    # the same oracle on one thread: one head of this workload, and the whole
-    # tiny fp32 ring workload (512 tokens, 4 heads, d 64, no mask)
+    t0 = time.perf_counter()
+    oracle.attention_ref(q[None], k[None], v[None], q_pos, np.arange(k.shape[0]), causal=True)
+    t_all = time.perf_counter() - t0
+    out = {"value": round(w["flops"] / t_all / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+           "kind": "oracle", "extrapolated": False,
+           "sample": f"the whole workload: rank-0 local queries (2048 tokens) x all 8192 keys, "
+                     f"{w['hq']} heads, float64 numpy, {t_all:.1f} s"}
     from threadpoolctl import threadpool_limits
     from seeded_inputs import CONFIGS, Q_ID, K_ID, V_ID
+    import torch
     c1 = CONFIGS[1]
     shape1 = (c1["batch"], c1["seq"], c1["heads"], c1["d"])
-    import torch
     q1, k1, v1 = (workloads.host_tensor(1, t, 0, shape1, torch.float32).cpu().numpy()
                   for t in (Q_ID, K_ID, V_ID))
     with threadpool_limits(limits=1):
@@ -465,6 +606,59 @@ def cpu_baseline(w):
     return out
 
 
+def cpu_baseline_decode():
+    """The oracle on one whole request of the decode workload (131,072 cached
+    tokens over 8 shards, 64 query heads): per-shard attention and the merge.
+    Rate in GB/s of the request's algorithmic bytes; the 64-request time is
+    extrapolated (x 64)."""
+    import torch
+    import ring_attention_02_amd as ra
+    import oracle
+    import workloads
+    from seeded_inputs import CONFIGS, Q_ID
+    c = CONFIGS[3]
+    B, hq, hkv, d, ctx = c["batch"], c["hq"], c["hkv"], c["d"], c["ctx"]
+    n_sh = c["pcp"] * c["dcp"]
+    kc, vc = workloads.decode_context(0)
+    k64, v64 = _host64(kc)[None], _host64(vc)[None]
+    del kc, vc
+    q64 = _host64(workloads.host_tensor(3, Q_ID, 0, (B, hq, d), torch.bfloat16)[:1])
+    dev, _ = ra.slot_mapping(np.arange(ctx), c["block_size"], c["interleave"], c["pcp"], c["dcp"])
+    t0 = time.perf_counter()
+    oracle.decode_shards_ref(q64, k64, v64, dev, n_sh)
+    t = time.perf_counter() - t0
+    nbytes = 2 * ctx * hkv * d * 2 + hq * d * 2 + 2 * n_sh * hq * (d + 1) * 4 + hq * (d + 1) * 4
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"request 0 of 64 (all 64 heads, 8 shards and the merge), float64 numpy, {t:.1f} s",
+            "extrapolated": True, "extrapolated_seconds_per_step": round(64 * t, 1)}
+
+
+def cpu_baseline_segmented(w):
+    """The oracle on 256 sampled (token, head) rows of the chunked-prefill
+    workload (4 heads x 64 query tokens, all keys up to the last row's
+    position), extrapolated to the whole workload by visible pairs."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(50505)
+    t_used, flops, rows = 0.0, 0, 0
+    for h in (0, 41, 86, w["h"] - 1):
+        k = _host64(w["k"][0, :, h])
+        v = _host64(w["v"][0, :, h])
+        off = np.sort(rng.choice(w["sq"], 64, replace=False))
+        qr = _host64(w["q"][0, torch.from_numpy(off).to(w["q"].device), h])
+        pos = w["q_pos0"] + off
+        n = int(pos.max()) + 1
+        t0 = time.perf_counter()
+        oracle.attention_ref(qr[None, :, None, :], k[None, :n, None, :], v[None, :n, None, :], pos,
+                             np.arange(n), causal=True)
+        t_used += time.perf_counter() - t0
+        flops += int((pos + 1).sum()) * (2 * w["dqk"] + 2 * w["dv"])
+        rows += len(pos)
+    rate = flops / t_used
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows} (token, head) rows (4 heads x 64 tokens), float64 numpy, {t_used:.1f} s",
+            "extrapolated": True, "extrapolated_seconds_per_step": round(w["flops"] / rate, 1)}
+
 
 def main():
     args = parse()
@@ -475,71 +669,71 @@ def main():
     import torch
     import ring_attention_02_amd  # noqa: F401  (fails loudly if the library is missing)
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.sweep_only:
-        sweep_only(args.sweep_only)
-        return
-    if args.decode_only:
-        decode_only(args.decode_only)
-        return
-    if args.merge_only:
-        merge_only(args.merge_only)
-        return
-    if args.long_step_only:
-        long_step_only(args.long_step_only)
-        return
+    for flag, fn in ((args.calibrate_copy, calibrate_copy), (args.sweep_only, sweep_only),
+                     (args.decode_only, decode_only), (args.merge_only, merge_only),
+                     (args.long_step_only, long_step_only), (args.long_sweep_only, long_sweep_only)):
+        if flag:
+            fn() if flag is True else fn(flag)
+            return
 
-    log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0")
-    w2, sec2, l2 = zigzag_bench(2, args.steps, args.warmup)
-    value = w2["flops"] / sec2 / 1e12
+    log(f"C4 (headline): zigzag causal prefill, 1M tokens, cp 8, rank 0: {args.warmup} + {args.steps} sweeps")
+    w4, sec4, l4 = long_headline(args.steps, args.warmup)
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec2 * 1e3, 4),
+        "metric": METRIC, "value": round(w4["flops"] / sec4 / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec4 * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "zigzag causal ring prefill, one rank's share: seq 8192, cp 4 "
-                               "(8 chunks of 1024), rank 0 holds Q chunks {0,7}, 32 heads, "
-                               "d 128, bf16",
-                   "global_batch": 1, "seq_len": 8192, "parallelism": "cp4 ring emulated on 1 GPU",
-                   "flops_per_step": w2["flops"]},
-        "roofline": roofline_entry("mfma", l2["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
-                                   profiled_traffic("attn_step_bf16_zigzag_seq8192_cp4.md",
+        "config": {"workload": "zigzag causal ring prefill, one rank's share of a 1,048,576-token "
+                               "sequence: cp 8 (16 chunks of 65,536), rank 0 holds Q chunks {0,15} "
+                               "(131,072 queries), 64 q-heads / 8 kv-heads, d 128, bf16",
+                   "global_batch": 1, "seq_len": 1048576, "parallelism": "cp8 ring emulated on 1 GPU",
+                   "flops_per_step": w4["flops"]},
+        "roofline": roofline_entry("mfma", l4["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                                   profiled_traffic("attn_step_bf16_long_prefill_1M_cp8_sweep.md",
                                                     "attn_step.hip")),
-        "kernel": {"name": "attn_step_bf16_kernel<128,128>",
-                   "mean_launch_ms": round(l2["mean_launch_ms"], 5),
-                   "launches_per_step": l2["launches_per_step"],
-                   "full_pair_ms": round(l2["full_ms"], 5), "diag_pair_ms": round(l2["diag_ms"], 5),
-                   "timing": "HIP-graph replay of the step's kernels back to back, HIP events"},
-        "launch": {"mode": "the K timed sweeps captured as one HIP graph and replayed once "
-                           "(one launch per ring step, next block's copy inside it)",
-                   "one_graph_per_sweep_ms_per_step": round(l2["per_graph_ms"], 4),
-                   "eager_ms_per_step": round(l2["eager_ms"], 4),
-                   "side_stream_copies_ms_per_step": round(l2["side_ms"], 4)},
+        "kernel": {"name": "attn_step_bf16_kernel<128,128,1,*,false,2> (7 FULL steps, 1 paired diagonal step)",
+                   "mean_launch_ms": round(l4["mean_launch_ms"], 3),
+                   "launches_per_step": l4["launches_per_step"],
+                   "full_step_ms": round(l4["full_ms"], 3), "diag_step_ms": round(l4["diag_ms"], 3),
+                   "timing": "HIP events around every launch of the timed sweeps, on the launch stream"},
+        "launch": {"mode": "one ring_attn_step_jobs launch per ring step, issued eagerly; each launch "
+                           "also copies the next K/V block into the idle staging slot",
+                   "full_step_traffic_bytes": profiled_traffic(
+                       "attn_step_bf16_long_prefill_1M_cp8_full_step.md", "attn_step.hip",
+                       field="full_step_traffic_bytes_per_launch")},
     }
-    del w2["ring"]
+    cpu = None
     if not args.no_cpu_baseline:
-        log("CPU baseline (oracle on host)")
-        out["cpu_baseline"] = cpu_baseline(w2)
-    del w2
+        log("CPU baseline: oracle on sampled rows of the 1M-token share")
+        cpu = cpu_baseline_long(w4)
+        out["cpu_baseline"] = cpu
+    del w4
     torch.cuda.empty_cache()
 
     if not args.primary_only:
         only = set(filter(None, args.only.split(",")))
-        sec = {}
-        if not only or "c4" in only:
-            log("C4: zigzag causal prefill, 1M tokens, cp 8, rank 0")
-            w4, s4, l4 = zigzag_bench(4, max(1, min(args.steps, 2)), 1, use_graph=False)
-            sec["long_prefill_1M_cp8"] = {
-                "value": round(w4["flops"] / s4 / 1e12, 3), "unit": "TFLOP/s",
-                "ms_per_step": round(s4 * 1e3, 3), "flops_per_step": w4["flops"],
-                "roofline": roofline_entry("mfma", l4["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
-                "full_pair_ms": round(l4["full_ms"], 3), "diag_pair_ms": round(l4["diag_ms"], 3),
-                "full_step_traffic_bytes": profiled_traffic(
-                    "attn_step_bf16_long_prefill_1M_cp8_full_step.md", "attn_step.hip",
-                    field="full_step_traffic_bytes_per_launch")}
-            del w4
+        sec, others = {}, {}
+        if not only or "c2" in only:
+            log("C2: zigzag causal prefill, seq 8192, cp 4, rank 0 (50 sweeps as one graph, 20 warm-up)")
+            w2, s2, l2 = short_zigzag_bench()
+            sec["short_prefill_8192_cp4"] = {
+                "value": round(w2["flops"] / s2 / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(s2 * 1e3, 4),
+                "flops_per_step": w2["flops"],
+                "roofline": roofline_entry("mfma", l2["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                                           profiled_traffic("attn_step_bf16_zigzag_seq8192_cp4.md",
+                                                            "attn_step.hip")),
+                "mean_launch_ms": round(l2["mean_launch_ms"], 5), "full_step_ms": round(l2["full_ms"], 5),
+                "diag_step_ms": round(l2["diag_ms"], 5),
+                "one_graph_per_sweep_ms": round(l2["per_graph_ms"], 4), "eager_ms": round(l2["eager_ms"], 4),
+                "side_stream_copies_ms": round(l2["side_ms"], 4),
+                "overlap": {"efficiency": round(l2["overlap"], 3), "t_sweep_ms": round(l2["t_sweep_ms"], 4),
+                            "t_compute_only_ms": round(l2["t_compute_ms"], 4),
+                            "t_copies_only_ms": round(l2["t_copy_ms"], 4),
+                            "definition": "(T_compute + T_copies - T_sweep) / T_copies, graph replays"}}
+            if cpu is not None:
+                log("CPU baseline: oracle on the whole 8192-token share")
+                others["short_prefill_8192_cp4"] = cpu_baseline_short(w2)
+            del w2
             torch.cuda.empty_cache()
         if not only or "c3" in only:
             log("C3: GQA decode, 64 x 131072 context, 8 shards")
@@ -552,6 +746,10 @@ def main():
                 "kernel_ms": round(l3["kernel_ms"], 4)}
             del w3
             torch.cuda.empty_cache()
+            if cpu is not None:
+                log("CPU baseline: oracle on one decode request")
+                others["decode_gqa_8_shards"] = cpu_baseline_decode()
+                torch.cuda.empty_cache()
         if not only or "c3p" in only:
             log("C3 paged: the same decode through per-request block tables")
             w3p, s3p, l3p = decode_bench(max(3, min(args.steps, 10)), 2, paged=True)
@@ -570,6 +768,9 @@ def main():
                 "ms_per_step": round(s5 * 1e3, 3), "flops_per_step": w5["flops"],
                 "roofline": roofline_entry("mfma", l5["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
                 "mean_launch_ms": round(l5["mean_launch_ms"], 4)}
+            if cpu is not None:
+                log("CPU baseline: oracle on sampled chunked-prefill rows")
+                others["segmented_prefill_mla"] = cpu_baseline_segmented(w5)
             del w5
             torch.cuda.empty_cache()
         if not only or "varlen" in only:
@@ -608,6 +809,8 @@ def main():
                 "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s",
                                            profiled_traffic("lse_merge_2x8M.md", "lse_merge.hip"))}
         out["secondary"] = sec
+        if cpu is not None and others:
+            cpu["others"] = others
     print(json.dumps(out), flush=True)
 
 
