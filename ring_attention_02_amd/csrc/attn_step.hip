@@ -259,7 +259,7 @@ struct FwdSlice {
 // waves per SIMD even when a launch has only one workgroup per CU.
 // ROWS = 2 (large grids): 8 waves own 256 query rows and share every K/V
 // tile, halving the tile loads and LDS writes per FLOP.
-template <int DQK, int DV, int SPLIT, bool PAIRED, bool VARLEN, int ROWS = 1>
+template <int DQK, int DV, int SPLIT, bool PAIRED, bool VARLEN, int ROWS, bool TAILS>
 __global__ void __launch_bounds__(kThreads * SPLIT * ROWS, 2)
 attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
@@ -456,19 +456,24 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   float m_run = kNegInf;  // running max of raw scores of this lane's row (possibly stale by < tau)
   float l_run = 0.f;      // running sum over this lane's half of the keys
 
-  // Direct buffer->LDS loads.  Each of K and V has a cursor: a buffer
-  // descriptor based at some tile of the current segment, whose record count
-  // ends at the segment's last key of this (batch, kv head), and the tile
-  // offset goes in the uniform soffset.  Rows past the end of the segment
-  // read as zeros (their scores are masked), so no tile needs a tail path.
-  // The range check of a raw buffer load covers the per-lane offset only,
-  // not the uniform soffset, so the segment's partial last tile is always
-  // loaded from a descriptor based at that tile (soffset 0): its rows past
-  // the end are then outside the record count.  The descriptor is rebuilt
-  // only when the sweep enters a segment, reaches that tile or has moved
-  // 2^30 bytes past its base.  Wave-instruction i fills 64 consecutive
-  // 16-byte LDS slots; each lane fetches the logical chunk the swizzle maps
-  // to its slot, at a loop-invariant byte offset inside the tile.
+  // Direct buffer->LDS loads.  Each of K and V has a cursor on the segment
+  // that holds the current tile; the segment's fields are read from the
+  // argument block only when the sweep enters it.  Wave-instruction i fills
+  // 64 consecutive 16-byte LDS slots; each lane fetches the logical chunk
+  // the swizzle maps to its slot, at a loop-invariant byte offset inside the
+  // tile.  Rows past the end of a segment must read as zeros (their scores
+  // are masked, but 0 * NaN in P V would still poison O), and the range
+  // check of a raw buffer load covers the per-lane offset only, not the
+  // uniform soffset:
+  //  * launches whose segments all hold whole 64-key tiles (TAILS false):
+  //    one descriptor per segment, based at some tile of it, the tile offset
+  //    in soffset; it is rebuilt when the sweep enters a segment or has
+  //    moved 2^30 bytes past its base.  No tile reaches past its segment.
+  //  * launches with a partial last tile somewhere (TAILS true): every tile
+  //    load uses a descriptor based at that tile, whose record count ends at
+  //    the segment's last key, so the rows past the end are out of range.
+  // (Building a descriptor per tile costs 0.5 scalar instructions per MFMA,
+  // which measured 4 % on long launches; hence the two forms.)
   const int64_t row_elems_k = static_cast<int64_t>(a.hkv) * DQK;
   const int64_t row_elems_v = static_cast<int64_t>(a.hkv) * DV;
   constexpr int KDMA_W = C::KDMA / ROWS, VDMA_W = C::VDMA / ROWS;   // per wave
@@ -490,54 +495,70 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   const int tile_bytes_v = static_cast<int>(kBN * row_elems_v * 2);
   const int rebase_k = (1 << 30) / tile_bytes_k, rebase_v = (1 << 30) / tile_bytes_v;
   struct DmaCursor {
-    int sg, start, end, base_vt, tail_vt;
-    __amdgpu_buffer_rsrc_t rsrc;
+    int sg, start, end;
+    int base_vt;                    // whole tiles: the descriptor's base tile
+    __amdgpu_buffer_rsrc_t rsrc;    // whole tiles: the segment's descriptor
+    const char* base;               // tails: the segment's key 0, this (batch, kv head)
+    int64_t valid;                  // tails: bytes from base to the end of key sk-1's row
   };
-  constexpr int kNoTail = 0x7FFFFFFF;
   auto seek = [&](DmaCursor& c, int vt, bool is_k) {
     advance(c.sg, c.start, c.end, vt);
     const int64_t sk = seg_sk(c.sg);
     const int64_t row_elems = is_k ? row_elems_k : row_elems_v;
     const int width = is_k ? DQK : DV;
     const uint16_t* base = seg_base(c.sg, is_k) + (static_cast<int64_t>(b) * sk * a.hkv + kvh) * width;
-    // the segment's partial last tile (rows past sk), if the sweep reaches it
-    c.tail_vt = sk % kBN != 0 ? c.start + static_cast<int>(sk / kBN) : kNoTail;
-    // a backward sweep bases the descriptor below vt so the next tiles reuse
-    // it; the partial last tile is based at itself
-    const int rebase = is_k ? rebase_k : rebase_v;
-    const int base_vt = rev && vt != c.tail_vt ? max(c.start, vt - rebase + 1) : vt;
-    const int64_t key0 = static_cast<int64_t>(base_vt - c.start) * kBN;
-    // bytes from the base tile to the end of key sk-1's row of this head
-    const int64_t valid = ((sk - 1 - key0) * row_elems + width) * 2;
-    const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
-    c.base_vt = base_vt;
-    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
-                                               static_cast<short>(0), nrec, 0x00020000);
+    if constexpr (TAILS) {
+      c.base = reinterpret_cast<const char*>(base);
+      c.valid = ((sk - 1) * row_elems + width) * 2;
+    } else {
+      // a backward sweep bases the descriptor below vt so the next tiles reuse it
+      const int rebase = is_k ? rebase_k : rebase_v;
+      const int base_vt = rev ? max(c.start, vt - rebase + 1) : vt;
+      const int64_t key0 = static_cast<int64_t>(base_vt - c.start) * kBN;
+      // bytes from the base tile to the end of key sk-1's row of this head
+      const int64_t valid = ((sk - 1 - key0) * row_elems + width) * 2;
+      const int nrec = valid > 0x7FFFFFF0 ? 0x7FFFFFF0 : static_cast<int>(valid);
+      c.base_vt = base_vt;
+      c.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * row_elems),
+                                                 static_cast<short>(0), nrec, 0x00020000);
+    }
+  };
+  // The descriptor and soffset of tile vt (moving the cursor first if needed).
+  auto tile_src = [&](DmaCursor& c, int vt, bool is_k, int* soff) {
+    if constexpr (TAILS) {
+      if (vt >= c.end || vt < c.start) seek(c, vt, is_k);
+      const int64_t off = static_cast<int64_t>(vt - c.start) * (is_k ? tile_bytes_k : tile_bytes_v);
+      const uint64_t left = static_cast<uint64_t>(c.valid - off);   // > 0: the tile holds a key
+      const int nrec = (left >> 31) != 0 ? 0x7FFFFFF0 : static_cast<int>(left);
+      *soff = 0;
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.base + off), static_cast<short>(0), nrec,
+                                               0x00020000);
+    } else {
+      if (vt >= c.end || vt < c.base_vt || vt - c.base_vt >= (is_k ? rebase_k : rebase_v)) seek(c, vt, is_k);
+      *soff = (vt - c.base_vt) * (is_k ? tile_bytes_k : tile_bytes_v);
+      return c.rsrc;
+    }
   };
   const auto no_rsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(nullptr), static_cast<short>(0), 0, 0);
-  DmaCursor kcur{-1, 0, 0, 0, kNoTail, no_rsrc}, vcur{-1, 0, 0, 0, kNoTail, no_rsrc};
+  DmaCursor kcur{-1, 0, 0, 0, no_rsrc, nullptr, 0}, vcur{-1, 0, 0, 0, no_rsrc, nullptr, 0};
   auto dma_k = [&](int vt, int stage) {
-    if (vt >= kcur.end || vt < kcur.base_vt || vt - kcur.base_vt >= rebase_k ||
-        (vt == kcur.tail_vt && vt != kcur.base_vt))
-      seek(kcur, vt, true);
-    const int soff = (vt - kcur.base_vt) * tile_bytes_k;
+    int soff;
+    const auto rsrc = tile_src(kcur, vt, true, &soff);
     uint16_t* dst = Kh + stage * C::KTILE;
 #pragma unroll
     for (int i = 0; i < KDMA_W; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          kcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
           static_cast<int>(koffb[i]), soff, 0, 0);
   };
   auto dma_v = [&](int vt, int stage) {
-    if (vt >= vcur.end || vt < vcur.base_vt || vt - vcur.base_vt >= rebase_v ||
-        (vt == vcur.tail_vt && vt != vcur.base_vt))
-      seek(vcur, vt, false);
-    const int soff = (vt - vcur.base_vt) * tile_bytes_v;
+    int soff;
+    const auto rsrc = tile_src(vcur, vt, false, &soff);
     uint16_t* dst = Vh + stage * C::VTILE;
 #pragma unroll
     for (int i = 0; i < VDMA_W; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vcur.rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * LW + wave) * 64 * 8), 16,
           static_cast<int>(voffb[i]), soff, 0, 0);
   };
 
@@ -995,8 +1016,8 @@ int device_cus() {
 
 // bf16 launch: a grid with fewer than two 4-wave workgroups per CU runs the
 // 8-wave key-split variant so every SIMD still holds two waves.
-template <int DQK, int DV>
-int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
+template <int DQK, int DV, bool TAILS>
+int32_t launch_bf16_t(JobArgs args, int64_t batch, hipStream_t stream) {
   const int64_t n_qtiles = (args.sq + kBM - 1) / kBM;
   const int64_t total = n_qtiles * (args.paired ? 1 : args.n_jobs) * args.hq * batch;
   RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
@@ -1010,10 +1031,10 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
       args.serp_w = xcd_cus;   // one 8-wave workgroup per CU
       if (args.paired)
-        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true, false>), grid, dim3(2 * kThreads), 0,
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, true, false, 1, TAILS>), grid, dim3(2 * kThreads), 0,
                            stream, args);
       else
-        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, false>), grid, dim3(2 * kThreads), 0,
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, false, 1, TAILS>), grid, dim3(2 * kThreads), 0,
                            stream, args);
       const hipError_t err = hipGetLastError();
       RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
@@ -1035,27 +1056,47 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
     bool launched = false;
     if constexpr (DQK <= 128) {
       if (args.paired) {
-        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, true, false, 2>), wide, dim3(2 * kThreads), 0,
+        hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, true, false, 2, TAILS>), wide, dim3(2 * kThreads), 0,
                            stream, args);
         launched = true;
       }
     }
     if (!launched)
-      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2>), wide, dim3(2 * kThreads), 0,
+      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 2, TAILS>), wide, dim3(2 * kThreads), 0,
                          stream, args);
   } else {
     args.serp_w = 2 * xcd_cus;   // two 4-wave workgroups per CU
-    hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, false, 1, TAILS>), grid, dim3(kThreads), 0, stream, args);
   }
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step: launch failed: %s", hipGetErrorString(err));
   return CP_OK;
 }
 
+// Does some segment end inside a 64-key tile?  Such launches run the
+// kernels that base a descriptor at every tile (TAILS).
+bool has_tails(const JobArgs& a) {
+  for (int j = 0; j < a.n_jobs; ++j)
+    for (int sg = 0; sg < a.job[j].n_seg; ++sg)
+      if (a.job[j].seg[sg].sk % kBN != 0) return true;
+  return false;
+}
+bool has_tails(const VarlenArgs& a) {
+  for (int r = 0; r < a.n_req; ++r)
+    if (a.req[r].k_len % kBN != 0) return true;
+  return false;
+}
+
+template <int DQK, int DV>
+int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
+  return has_tails(args) ? launch_bf16_t<DQK, DV, true>(args, batch, stream)
+                         : launch_bf16_t<DQK, DV, false>(args, batch, stream);
+}
+
 // Varlen launch: every (query tile up to the longest request, request,
 // head); tiles past a request's end exit at once.
-template <int DQK, int DV>
-int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
+template <int DQK, int DV, bool TAILS>
+int32_t launch_bf16_varlen_t(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   const int64_t n_qtiles = (max_q + kBM - 1) / kBM;
   const int64_t total = n_qtiles * args.n_req * args.base.hq;
   RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
@@ -1068,7 +1109,7 @@ int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   if constexpr (DQK <= 128) {
     if (total < 2 * static_cast<int64_t>(device_cus())) {
       args.base.serp_w = xcd_cus;
-      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, true>), grid, dim3(2 * kThreads), 0,
+      hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 2, false, true, 1, TAILS>), grid, dim3(2 * kThreads), 0,
                          stream, args);
       const hipError_t err = hipGetLastError();
       RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));
@@ -1078,10 +1119,16 @@ int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   // (128-row tiles here: packed requests end on ragged rows, which 256-row
   // tiles waste -- measured slower for the varlen mix.)
   args.base.serp_w = 2 * xcd_cus;
-  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, true>), grid, dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((attn_step_bf16_kernel<DQK, DV, 1, false, true, 1, TAILS>), grid, dim3(kThreads), 0, stream, args);
   const hipError_t err = hipGetLastError();
   RA_CHECK(err == hipSuccess, CP_EHIP, "ring_attn_step_varlen: launch failed: %s", hipGetErrorString(err));
   return CP_OK;
+}
+
+template <int DQK, int DV>
+int32_t launch_bf16_varlen(VarlenArgs args, int64_t max_q, hipStream_t stream) {
+  return has_tails(args) ? launch_bf16_varlen_t<DQK, DV, true>(args, max_q, stream)
+                         : launch_bf16_varlen_t<DQK, DV, false>(args, max_q, stream);
 }
 
 int32_t launch_bf16_any(int32_t d_qk, JobArgs args, int64_t batch, hipStream_t stream) {

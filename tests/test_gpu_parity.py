@@ -795,6 +795,12 @@ SERPENTINE = [
     (768, 650, 128, 16, 64, 64, 400, 100),     # 4-wave, 2 rounds
     (1000, 520, 256, 32, 128, 128, 200, 0),    # 256-row, 4 rounds, ragged rows
     (1000, 300, 256, 256, 192, 128, 250, 100), # 256-row d 192
+    # the same launch forms with whole 64-key tiles only (the kernels that keep
+    # one descriptor per segment; the ragged cases above run the per-tile ones)
+    (384, 704, 96, 96, 128, 128, 300, 0),
+    (768, 640, 128, 16, 64, 64, 400, 100),
+    (1000, 512, 256, 32, 128, 128, 200, 0),
+    (1000, 320, 256, 256, 192, 128, 250, 100),
 ]
 
 
