@@ -350,6 +350,25 @@ int32_t split_kv_decode(const void* q, const void* k_shards, const void* v_shard
                         void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * split_kv_decode_noalloc -- split_kv_decode without a caller workspace.
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * key-split partials go to a static device array of the library instead
+ * (40 MiB, held by each GPU the library runs on until the process ends),
+ * and the call itself allocates nothing.  Arguments, layouts, results and
+ * errors are those of split_kv_decode (same kernels); a shape whose splits
+ * would need more than the array is CP_EUNSUPPORTED (no supported shape
+ * does).  Calls on one GPU share its array: calls that overlap in time on
+ * one GPU (different streams without ordering) race; calls ordered on one
+ * stream are safe, since every call rewrites what it reads.
+ * ---------------------------------------------------------------------- */
+int32_t split_kv_decode_noalloc(const void* q, const void* k_shards, const void* v_shards,
+                                int32_t dtype, int32_t n_shards, int32_t batch, int64_t t_shard,
+                                const int64_t* shard_lens, int32_t hq, int32_t hkv, int32_t d_qk,
+                                int32_t d_v, float scale, float* o_parts, float* lse_parts,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * split_kv_decode_paged -- split_kv_decode over a paged KV cache.
  * [CP] "How it works / Block table": a request's logical KV blocks map to
  * physical blocks of the device's cache through its block table, and the

@@ -28,7 +28,7 @@ EXPORTED = ("cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition
             "cp_slot_mapping", "cp_classify", "ring_attn_step", "lse_merge",
             "split_kv_decode_workspace", "split_kv_decode", "ring_stage_copy",
             "ring_attn_step_jobs", "split_kv_decode_paged", "ring_attn_step_varlen",
-            "cp_gather_rows", "cp_reorg_index", "cp_ring_schedule")
+            "cp_gather_rows", "cp_reorg_index", "cp_ring_schedule", "split_kv_decode_noalloc")
 
 
 class RingAttnError(RuntimeError):
@@ -70,6 +70,9 @@ _lib.split_kv_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64]
 _lib.split_kv_decode.restype = _i32
 _lib.split_kv_decode.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i32, _i32, _i32,
                                  _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+_lib.split_kv_decode_noalloc.restype = _i32
+_lib.split_kv_decode_noalloc.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _i32, _i32, _i32,
+                                         _i32, _f32, _vp, _vp, _vp]
 _lib.split_kv_decode_paged.restype = _i32
 _lib.split_kv_decode_paged.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                        _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
@@ -372,6 +375,32 @@ def split_kv_decode(q, k_shards, v_shards, shard_lens=None, scale=None, o_parts=
     return o_parts, lse_parts
 
 
+def split_kv_decode_noalloc(q, k_shards, v_shards, o_parts, lse_parts, shard_lens=None, scale=None,
+                            stream=None):
+    """split_kv_decode into caller-given o_parts / lse_parts, with the key-split
+    partials in the library's static scratch array: the call allocates nothing."""
+    B, Hq, Dqk = q.shape
+    S, Bk, T, Hkv, Dk = k_shards.shape
+    Dv = v_shards.shape[4]
+    if Bk != B or Dk != Dqk or tuple(v_shards.shape[:4]) != (S, B, T, Hkv):
+        raise ValueError("q / shard shapes do not agree")
+    if tuple(o_parts.shape) != (S, B, Hq, Dv) or tuple(lse_parts.shape) != (S, B, Hq):
+        raise ValueError("o_parts must be [S, B, Hq, Dv] and lse_parts [S, B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    lens_ptr = None
+    if shard_lens is not None:
+        if tuple(shard_lens.shape) != (S, B):
+            raise ValueError("shard_lens must be int64 [n_shards, batch]")
+        lens_ptr = _dev_ptr(shard_lens, "shard_lens")
+    _check(_lib.split_kv_decode_noalloc(_dev_ptr(q, "q"), _dev_ptr(k_shards, "k_shards"),
+                                        _dev_ptr(v_shards, "v_shards"), _dtype_code(q), S, B, T, lens_ptr,
+                                        Hq, Hkv, Dqk, Dv, float(scale), _dev_ptr(o_parts, "o_parts"),
+                                        _dev_ptr(lse_parts, "lse_parts"), _stream_handle(stream)),
+           "split_kv_decode_noalloc")
+    return o_parts, lse_parts
+
+
 def split_kv_decode_paged(q, k_pool, v_pool, block_tables, shard_lens, scale=None, o_parts=None,
                           lse_parts=None, workspace=None, stream=None):
     """Per-shard decode partials over paged caches.
@@ -484,6 +513,7 @@ from .ring import ZigzagRing, segmented_prefill, noncausal_ring_sweep  # noqa: E
 __all__ = ["partition", "slot_mapping", "reorg_index", "ring_schedule", "classify", "ring_attn_step", "ring_attn_step_jobs",
            "lse_merge", "stage_copy",
            "split_kv_decode", "split_kv_decode_workspace", "split_kv_decode_paged",
+           "split_kv_decode_noalloc",
            "ring_attn_step_varlen", "gather_rows", "ZigzagRing", "segmented_prefill",
            "noncausal_ring_sweep", "RingAttnError", "FULL", "DIAG", "SKIP", "EXPORTED", "lib",
            "last_error"]

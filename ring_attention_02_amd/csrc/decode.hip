@@ -18,8 +18,18 @@
 // to fill the GPU) are merged by the LSE merge kernel.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels_common.h"
 #include "status.h"
+
+// Key-split workspace of split_kv_decode_noalloc: a static device array
+// instead of caller memory.  Every supported shape fits (d_v = 128, at most
+// 16 query heads per kv head, splits only below 2,048 work items: at most
+// 4,094 x 16 rows x 129 floats = 33.8 MB).  Each GPU the library runs on
+// holds its own copy until the process ends.
+static constexpr size_t kScratchBytes = size_t{40} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace ringattn {
 
@@ -397,6 +407,51 @@ extern "C" int32_t split_kv_decode(const void* q, const void* k_shards, const vo
   args.scale = scale;
   return run_decode("split_kv_decode", false, args, dtype, d_qk, d_v, o_parts, lse_parts, workspace,
                     ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current (the array's name in host code is only a stand-in).
+int32_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  RA_CHECK(err == hipSuccess && dev >= 0 && dev < kMaxDevices, CP_EHIP,
+           "split_kv_decode_noalloc: no current device (%s)", hipGetErrorString(err));
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    RA_CHECK(err == hipSuccess && p != nullptr, CP_EHIP,
+             "split_kv_decode_noalloc: hipGetSymbolAddress of the scratch array failed: %s",
+             hipGetErrorString(err));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return CP_OK;
+}
+}  // namespace
+
+extern "C" int32_t split_kv_decode_noalloc(const void* q, const void* k_shards, const void* v_shards,
+                                           int32_t dtype, int32_t n_shards, int32_t batch,
+                                           int64_t t_shard, const int64_t* shard_lens, int32_t hq,
+                                           int32_t hkv, int32_t d_qk, int32_t d_v, float scale,
+                                           float* o_parts, float* lse_parts, void* stream) {
+  // Every split's partial is written in full before the merge reads it, so
+  // nothing left in the array by an earlier call is ever read.
+  const size_t need = split_kv_decode_workspace(n_shards, batch, hq, hkv, d_v, t_shard);
+  RA_CHECK(need <= kScratchBytes, CP_EUNSUPPORTED,
+           "split_kv_decode_noalloc: %zu bytes of key-split scratch needed, the static array holds %zu",
+           need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int32_t rc = scratch_address(&ws);
+    if (rc != CP_OK) return rc;
+  }
+  return split_kv_decode(q, k_shards, v_shards, dtype, n_shards, batch, t_shard, shard_lens, hq, hkv,
+                         d_qk, d_v, scale, o_parts, lse_parts, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 extern "C" int32_t split_kv_decode_paged(const void* q, const void* k_pool, const void* v_pool,
