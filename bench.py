@@ -63,6 +63,14 @@ def parse():
                    help="only run one FULL ring-step launch of the 1M-token prefill K times")
     p.add_argument("--long-sweep-only", type=int, default=0, metavar="K",
                    help="only run K sweeps of the 1M-token prefill (for counter passes)")
+    p.add_argument("--paged-only", type=int, default=0, metavar="K",
+                   help="only run the paged decode kernel K times (for counter passes)")
+    p.add_argument("--segmented-only", type=int, default=0, metavar="K",
+                   help="only run the chunked prefill (MLA shape) K times (for counter passes)")
+    p.add_argument("--varlen-only", type=int, default=0, metavar="K",
+                   help="only run the packed 16-request prefill launch K times (for counter passes)")
+    p.add_argument("--reorg-only", type=int, default=0, metavar="K",
+                   help="only run the reorganisation gather (K then V) K times (for counter passes)")
     return p.parse_args()
 
 
@@ -94,6 +102,79 @@ def decode_only(reps):
                            lse_parts=lse_parts)
     torch.cuda.synchronize()
     print(json.dumps({"decode_launches": reps, "kernel_bytes": decode_kernel_bytes(w)}), flush=True)
+
+
+def paged_only(reps):
+    """The paged decode kernel alone, K launches (no merge)."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.decode_paged_setup()
+    o_parts = torch.empty((w["n_shards"], w["B"], w["hq"], w["d"]), device="cuda")
+    lse_parts = torch.empty((w["n_shards"], w["B"], w["hq"]), device="cuda")
+    for _ in range(reps):
+        ra.split_kv_decode_paged(w["q"], w["kp"], w["vp"], w["tables"], w["lens"], o_parts=o_parts,
+                                 lse_parts=lse_parts)
+    torch.cuda.synchronize()
+    print(json.dumps({"paged_decode_launches": reps, "kernel_bytes": decode_kernel_bytes(w)}), flush=True)
+
+
+def segmented_only(reps):
+    """The chunked prefill (MLA shape) alone, K times (5 ring-step launches each)."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.segmented_setup()
+    for _ in range(reps):
+        ra.segmented_prefill(w["q"], w["k"], w["v"], w["o"], w["lse"], q_pos0=w["q_pos0"], segment=w["segment"])
+    torch.cuda.synchronize()
+    print(json.dumps({"segmented_runs": reps, "bytes_per_run": segmented_bytes(w)}), flush=True)
+
+
+def segmented_bytes(w):
+    """Algorithmic bytes of one chunked prefill: Q once per launch (up to four
+    segments each), every K/V byte once, O and LSE written by the first launch
+    and read and written by each later one."""
+    n_seg = -(-w["skv"] // w["segment"])
+    launches = -(-n_seg // 4)
+    q = w["sq"] * w["h"] * w["dqk"] * 2
+    kv = w["skv"] * w["h"] * (w["dqk"] + w["dv"]) * 2
+    ol = w["sq"] * w["h"] * (w["dv"] + 1) * 4
+    return launches * q + kv + ol + (launches - 1) * 2 * ol
+
+
+def varlen_only(reps):
+    """The packed 16-request prefill launch alone, K times."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.varlen_setup()
+    for _ in range(reps):
+        ra.ring_attn_step_varlen(w["q"], w["k"], w["v"], w["cu"], w["cu"], w["pos"], w["pos"],
+                                 o=w["o"], lse=w["lse"], causal=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"varlen_launches": reps, "bytes_per_launch": varlen_bytes(w)}), flush=True)
+
+
+def varlen_bytes(w):
+    """Algorithmic bytes of the packed launch: Q, K and V read once, O and LSE written."""
+    t = int(w["cu"][-1])
+    return t * (w["hq"] * w["d"] * 2 + 2 * w["hkv"] * w["d"] * 2 + w["hq"] * (w["d"] + 1) * 4)
+
+
+def reorg_only(reps):
+    """The reorganisation gather alone: K then V rows, K times."""
+    import torch
+    import ring_attention_02_amd as ra
+    import workloads
+    w = workloads.reorg_setup()
+    ok = torch.empty_like(w["gk"])
+    ov = torch.empty_like(w["gv"])
+    for _ in range(reps):
+        ra.gather_rows(w["gk"], w["idx"], dst=ok)
+        ra.gather_rows(w["gv"], w["idx"], dst=ov)
+    torch.cuda.synchronize()
+    print(json.dumps({"gather_pairs": reps, "bytes_per_pair": w["bytes"]}), flush=True)
 
 
 def decode_kernel_bytes(w):
@@ -671,7 +752,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     for flag, fn in ((args.calibrate_copy, calibrate_copy), (args.sweep_only, sweep_only),
                      (args.decode_only, decode_only), (args.merge_only, merge_only),
-                     (args.long_step_only, long_step_only), (args.long_sweep_only, long_sweep_only)):
+                     (args.long_step_only, long_step_only), (args.long_sweep_only, long_sweep_only),
+                     (args.paged_only, paged_only), (args.segmented_only, segmented_only),
+                     (args.varlen_only, varlen_only), (args.reorg_only, reorg_only)):
         if flag:
             fn() if flag is True else fn(flag)
             return
@@ -756,7 +839,8 @@ def main():
             sec["decode_gqa_8_shards_paged"] = {
                 "value": round(w3p["bytes"] / s3p / 1e9, 1), "unit": "GB/s",
                 "ms_per_step": round(s3p * 1e3, 4), "bytes_per_step": w3p["bytes"],
-                "roofline": roofline_entry("hbm", l3p["kernel_gbs"], PEAK_HBM_GBS, "GB/s"),
+                "roofline": roofline_entry("hbm", l3p["kernel_gbs"], PEAK_HBM_GBS, "GB/s",
+                                           profiled_traffic("decode_bf16_gqa_8shards_paged.md", "decode.hip")),
                 "kernel_ms": round(l3p["kernel_ms"], 4)}
             del w3p
             torch.cuda.empty_cache()
@@ -766,7 +850,9 @@ def main():
             sec["segmented_prefill_mla"] = {
                 "value": round(w5["flops"] / s5 / 1e12, 3), "unit": "TFLOP/s",
                 "ms_per_step": round(s5 * 1e3, 3), "flops_per_step": w5["flops"],
-                "roofline": roofline_entry("mfma", l5["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+                "roofline": roofline_entry("mfma", l5["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                                           profiled_traffic("attn_step_bf16_segmented_prefill_mla.md",
+                                                            "attn_step.hip")),
                 "mean_launch_ms": round(l5["mean_launch_ms"], 4)}
             if cpu is not None:
                 log("CPU baseline: oracle on sampled chunked-prefill rows")
@@ -780,7 +866,8 @@ def main():
                 "value": round(w7["flops"] / s7 / 1e12, 3), "unit": "TFLOP/s",
                 "ms_per_step": round(s7 * 1e3, 4), "flops_per_step": w7["flops"],
                 "tokens": int(w7["cu"][-1]),
-                "roofline": roofline_entry("mfma", l7["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"),
+                "roofline": roofline_entry("mfma", l7["achieved_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                                           profiled_traffic("attn_step_bf16_varlen_16req.md", "attn_step.hip")),
                 "mean_launch_ms": round(l7["mean_launch_ms"], 4)}
             del w7
             torch.cuda.empty_cache()
@@ -790,7 +877,8 @@ def main():
             sec["reorg_kvcache_gather"] = {
                 "value": round(w8["bytes"] / s8 / 1e9, 1), "unit": "GB/s",
                 "ms_per_step": round(s8 * 1e3, 4), "bytes_per_step": w8["bytes"],
-                "roofline": roofline_entry("hbm", w8["bytes"] / s8 / 1e9, PEAK_HBM_GBS, "GB/s")}
+                "roofline": roofline_entry("hbm", w8["bytes"] / s8 / 1e9, PEAK_HBM_GBS, "GB/s",
+                                           profiled_traffic("gather_rows_reorg_kvcache.md", "stage.hip"))}
             del w8
             torch.cuda.empty_cache()
         if not only or "c1" in only:

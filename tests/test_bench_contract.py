@@ -27,6 +27,17 @@ def test_profiled_traffic_matches_the_committed_summary():
         assert 1e8 < t < 2e8
 
 
+def test_long_sweep_traffic_matches_the_committed_summary():
+    sys.path.insert(0, ROOT)
+    import bench
+    t = bench.profiled_traffic("attn_step_bf16_long_prefill_1M_cp8_sweep.md", "attn_step.hip")
+    text = open(os.path.join(ROOT, "profiles", "attn_step_bf16_long_prefill_1M_cp8_sweep.md")).read()
+    assert "traffic_bytes_per_launch:" in text and "--long-sweep-only 1" in text
+    if t is not None:
+        # at least the algorithmic bytes of a sweep launch (7.01 GB), re-reads below L2 included
+        assert 7.0e9 < t < 1.0e11
+
+
 def test_decode_traffic_matches_the_committed_summary():
     sys.path.insert(0, ROOT)
     import bench
