@@ -548,6 +548,50 @@ def merge_bench(steps, warmup):
     return sec, nbytes
 
 
+def context_bench():
+    """What the same GPU reaches on work with nothing but the roofline in the
+    way, measured in the same run: a bf16 GEMM of 8192^3 through torch.matmul
+    (the vendor BLAS; 300 back-to-back calls after 100 warm-up calls, long
+    enough for the clock to settle as under the prefill sweeps) and a plain
+    1 GiB device-to-device copy (read + write bytes).  Not part of the path:
+    it puts the kernels' roofline fractions next to a practical ceiling."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(100):
+        torch.matmul(a, b, out=c)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls = 300
+    s.record()
+    for _ in range(calls):
+        torch.matmul(a, b, out=c)
+    e.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 / (s.elapsed_time(e) * 1e-3 / calls) / 1e12
+    del a, b, c
+    src = torch.empty(1 << 29, device="cuda", dtype=torch.int16)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    s.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (s.elapsed_time(e) * 1e-3 / 20) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_8192": {"tflops": round(gemm_tflops, 1),
+                               "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                               "what": "torch.matmul bf16 8192x8192x8192, 300 calls after 100 warm-up"},
+            "d2d_copy_1GiB": {"gbs": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+                              "what": "1 GiB device-to-device tensor copy, read + write bytes"}}
+
+
 def long_step_only(reps):
     """One FULL ring step of the 1M-token zigzag prefill (rank 0, cp 8): the
     launch that attends the tail query part to a whole staged block and
@@ -897,6 +941,9 @@ def main():
                 "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s",
                                            profiled_traffic("lse_merge_2x8M.md", "lse_merge.hip"))}
         out["secondary"] = sec
+        if not only or "context" in only:
+            log("context: vendor bf16 GEMM and a plain device copy on the same GPU")
+            out["context"] = context_bench()
         if cpu is not None and others:
             cpu["others"] = others
     print(json.dumps(out), flush=True)
