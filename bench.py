@@ -369,8 +369,12 @@ def long_headline(steps, warmup):
     full_ms = float(np.mean([d for c, d in durs if c == ra.FULL]))
     diag = [d for c, d in durs if c == ra.DIAG]
     flops_per_launch = w["flops"] / launches
+    # The ring transfer's share: the sweep's forwarded blocks copied alone
+    # (ring_stage_copy launches, one HIP graph), against the sweep.
+    copies = [lambda u=u: ra.stage_copy(ring.forward_pairs(u)) for u in range(1, ring.cp)]
+    t_copy_ms = graph_ms(copies, 1, 3)
     return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=launches,
-                        flops_per_launch=flops_per_launch,
+                        flops_per_launch=flops_per_launch, t_copy_ms=t_copy_ms,
                         achieved_tflops=flops_per_launch / (mean_ms * 1e-3) / 1e12,
                         full_ms=full_ms, diag_ms=float(np.mean(diag)) if diag else None)
 
@@ -426,8 +430,11 @@ def short_zigzag_bench(sweeps=50, warmup=20):
 
 def tiny_bench(steps, warmup):
     """C1: the fp32 non-causal ring, 512 tokens in 4 blocks of 128, 4 heads,
-    d 64: 16 ring-step launches and one 4-part LSE merge per sweep, issued
-    eagerly (a correctness workload: the figure is mostly launch cost)."""
+    d 64: 16 ring-step launches and one 4-part LSE merge per sweep (a
+    correctness workload: each fp32 launch is 8 one-wave workgroups, so
+    the sweep is bound by the latency of single waves, not by the ALU or by
+    launch issue).  Returns the graph-replayed and the eager seconds per
+    sweep."""
     import torch
     import ring_attention_02_amd as ra
     import workloads
@@ -436,8 +443,21 @@ def tiny_bench(steps, warmup):
     shape = (c["batch"], c["seq"], c["heads"], c["d"])
     q, k, v = (workloads.host_tensor(1, t, 0, shape, torch.float32) for t in (Q_ID, K_ID, V_ID))
     flops = c["batch"] * c["seq"] * c["seq"] * c["heads"] * 4 * c["d"]
-    sec = time_steps(lambda: ra.noncausal_ring_sweep(q, k, v, c["n_blocks"]), steps, warmup)
-    return flops, sec
+    sweep = lambda: ra.noncausal_ring_sweep(q, k, v, c["n_blocks"])
+    eager = time_steps(sweep, steps, warmup)
+    # the same sweep (its 16 step launches, their K/V block copies and the
+    # merge) recorded once as a HIP graph and replayed once per timed step
+    torch.cuda.synchronize()
+    graph, stream = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        sweep()
+        with torch.cuda.graph(graph, stream=stream):
+            sweep()
+    torch.cuda.synchronize()
+    graph_upload(graph)
+    sec = time_steps(graph.replay, steps, warmup)
+    return flops, sec, eager
 
 
 def decode_bench(steps, warmup, paged=False):
@@ -649,42 +669,46 @@ def _host64(t):
 
 
 def cpu_baseline_long(w):
-    """The oracle on 512 sampled (token, head) rows of the 1M-token rank-0
-    share, extrapolated to the whole sweep by visible-pair count.
+    """The oracle on 3,072 sampled (token, head) rows of the 1M-token rank-0
+    share (about 10 s of host work), extrapolated to the whole sweep by
+    visible-pair count.
 
-    Rows: 2 kv heads (the first and the last) x 4 of their query heads x 64
-    tokens, 32 of each local Q chunk at seeded random offsets.  Each batch of
-    32 rows goes to the oracle with the keys up to its last row's position,
-    causal by absolute position, so it computes (and masks) at least the
-    visible pairs it is credited with.  Only the oracle calls are timed."""
+    Rows: 4 kv heads (0, 3, 4 and 7) x 4 of their query heads x 192 tokens,
+    96 of each local Q chunk at seeded random offsets, in batches of 32.
+    Each batch goes to the oracle with the keys up to its last row's
+    position, causal by absolute position, so it computes (and masks) at
+    least the visible pairs it is credited with.  Only the oracle calls are
+    timed."""
     import torch
     import oracle
     rng = np.random.default_rng(40404)
     c, d, hq, hkv = w["chunk"], w["d"], w["hq"], w["hkv"]
     group = hq // hkv
     t_used, flops, rows = 0.0, 0, 0
-    for kvh in (0, hkv - 1):
+    kv_heads = sorted({0, (hkv - 1) // 2, hkv // 2, hkv - 1})
+    for kvh in kv_heads:
         k = _host64(w["k_full"][0, :, kvh])
         v = _host64(w["v_full"][0, :, kvh])
         for h in kvh * group + np.array([0, 3, 5, 7]) % group:
             for i, part in enumerate(w["local_parts"]):
-                off = np.sort(rng.choice(c, 32, replace=False))
-                idx = torch.from_numpy(i * c + off).to(w["q_local"].device)
-                qr = _host64(w["q_local"][0, idx, int(h)])               # [32, d]
-                pos = part * c + off
-                n = int(pos.max()) + 1
-                t0 = time.perf_counter()
-                oracle.attention_ref(qr[None, :, None, :], k[None, :n, None, :], v[None, :n, None, :],
-                                     pos, np.arange(n), causal=True)
-                t_used += time.perf_counter() - t0
-                flops += int((pos + 1).sum()) * (2 * d + 2 * d)
-                rows += len(pos)
+                offs = np.sort(rng.choice(c, 96, replace=False))
+                for off in np.split(offs, 3):
+                    idx = torch.from_numpy(i * c + off).to(w["q_local"].device)
+                    qr = _host64(w["q_local"][0, idx, int(h)])               # [32, d]
+                    pos = part * c + off
+                    n = int(pos.max()) + 1
+                    t0 = time.perf_counter()
+                    oracle.attention_ref(qr[None, :, None, :], k[None, :n, None, :], v[None, :n, None, :],
+                                         pos, np.arange(n), causal=True)
+                    t_used += time.perf_counter() - t0
+                    flops += int((pos + 1).sum()) * (2 * d + 2 * d)
+                    rows += len(pos)
         del k, v
     rate = flops / t_used
     return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"{rows} (token, head) rows of the 1M-token rank-0 share (2 kv heads x 4 query heads x "
-                      f"32 tokens of each local chunk), float64 numpy, {t_used:.1f} s; the rate is "
-                      f"extrapolated to the whole sweep by visible pairs",
+            "sample": f"{rows} (token, head) rows of the 1M-token rank-0 share ({len(kv_heads)} kv heads x 4 "
+                      f"query heads x 96 tokens of each local chunk), float64 numpy, {t_used:.1f} s; the "
+                      f"rate is extrapolated to the whole sweep by visible pairs",
             "extrapolated": True, "extrapolated_seconds_per_sweep": round(w["flops"] / rate, 1),
             **host_cores()}
 
@@ -825,6 +849,8 @@ def main():
                    "timing": "HIP events around every launch of the timed sweeps, on the launch stream"},
         "launch": {"mode": "one ring_attn_step_jobs launch per ring step, issued eagerly; each launch "
                            "also copies the next K/V block into the idle staging slot",
+                   "forwarded_blocks_alone_ms": round(l4["t_copy_ms"], 3),
+                   "forwarded_share_of_sweep": round(l4["t_copy_ms"] / (sec4 * 1e3), 5),
                    "full_step_traffic_bytes": profiled_traffic(
                        "attn_step_bf16_long_prefill_1M_cp8_full_step.md", "attn_step.hip",
                        field="full_step_traffic_bytes_per_launch")},
@@ -927,12 +953,14 @@ def main():
             torch.cuda.empty_cache()
         if not only or "c1" in only:
             log("C1: tiny non-causal ring, fp32, 512 tokens in 4 blocks")
-            f1, s1 = tiny_bench(max(10, args.steps), 5)
+            f1, s1, e1 = tiny_bench(max(10, args.steps), 5)
             sec["tiny_noncausal_ring_f32"] = {
                 "value": round(f1 / s1 / 1e12, 4), "unit": "TFLOP/s", "ms_per_step": round(s1 * 1e3, 4),
-                "flops_per_step": f1,
+                "flops_per_step": f1, "eager_ms": round(e1 * 1e3, 4),
                 "roofline": roofline_entry("alu", f1 / s1 / 1e12, PEAK_F32_VALU_TFLOPS, "TFLOP/s"),
-                "note": "correctness workload: 16 launches and one merge per sweep, issued eagerly"}
+                "note": "correctness workload: 16 step launches of 8 one-wave workgroups and one merge per "
+                        "sweep, replayed as one HIP graph per sweep (eager_ms: the same sweep issued "
+                        "eagerly)"}
         if not only or "merge" in only:
             log("lse_merge: 2 partials x 8.4M rows x 128")
             s6, b6 = merge_bench(max(5, args.steps), 2)
