@@ -269,18 +269,29 @@ def time_steps(step_fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def build_digest(source):
+    """The build digest of a kernel source file (its bytes and device flags),
+    as the package's build script computes it."""
+    import importlib.util
+    root = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location(
+        "_ringattn_build", os.path.join(root, "ring_attention_02_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.build_digest(source)
+
+
 def profiled_traffic(summary, source, field="traffic_bytes_per_launch"):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel source changed after the counters were taken."""
-    import hashlib
+    when the kernel's source or its compile flags changed after the counters
+    were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         text = open(os.path.join(root, "profiles", summary)).read()
-        src = open(os.path.join(root, "ring_attention_02_amd", "csrc", source), "rb").read()
+        sha = build_digest(source)
     except OSError:
         return None
-    sha = hashlib.sha256(src).hexdigest()[:16]
-    key = f"kernel source sha256 prefix ({source})"
+    key = f"kernel build sha256 prefix ({source})"
     fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and
                   line.split(": ", 1)[0] in (key, field))
     if fields.get(key, "").strip() != sha or field not in fields:
@@ -431,10 +442,9 @@ def short_zigzag_bench(sweeps=50, warmup=20):
 def tiny_bench(steps, warmup):
     """C1: the fp32 non-causal ring, 512 tokens in 4 blocks of 128, 4 heads,
     d 64: 16 ring-step launches and one 4-part LSE merge per sweep (a
-    correctness workload: each fp32 launch is 8 one-wave workgroups, so
-    the sweep is bound by the latency of single waves, not by the ALU or by
-    launch issue).  Returns the graph-replayed and the eager seconds per
-    sweep."""
+    correctness workload: each fp32 launch is 8 workgroups of 64 rows, so
+    the sweep is bound by latency, not by the ALU or by launch issue).
+    Returns the graph-replayed and the eager seconds per sweep."""
     import torch
     import ring_attention_02_amd as ra
     import workloads
@@ -958,9 +968,9 @@ def main():
                 "value": round(f1 / s1 / 1e12, 4), "unit": "TFLOP/s", "ms_per_step": round(s1 * 1e3, 4),
                 "flops_per_step": f1, "eager_ms": round(e1 * 1e3, 4),
                 "roofline": roofline_entry("alu", f1 / s1 / 1e12, PEAK_F32_VALU_TFLOPS, "TFLOP/s"),
-                "note": "correctness workload: 16 step launches of 8 one-wave workgroups and one merge per "
-                        "sweep, replayed as one HIP graph per sweep (eager_ms: the same sweep issued "
-                        "eagerly)"}
+                "note": "correctness workload: 16 step launches of 8 workgroups (64 rows, 4 key-split "
+                        "waves) and one merge per sweep, replayed as one HIP graph per sweep (eager_ms: "
+                        "the same sweep issued eagerly)"}
         if not only or "merge" in only:
             log("lse_merge: 2 partials x 8.4M rows x 128")
             s6, b6 = merge_bench(max(5, args.steps), 2)

@@ -865,14 +865,29 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
 // ---------------------------------------------------------------------------
 // float32 vector kernel (correctness path for float32 inputs)
 // ---------------------------------------------------------------------------
-constexpr int kF32Rows = 64;  // one query row per lane, one wave per workgroup
-constexpr int kF32Keys = 32;
+// One query row per lane: a workgroup holds 64 rows of one (batch, head) in
+// each of its 4 waves, and wave w sweeps key tiles w, w + 4, ... with its own
+// running max, sum and output, staged through its own LDS tile.  The four
+// states are merged by the running-max rule at the end (the same online
+// softmax, applied across the key split).
+constexpr int kF32Rows = 64;   // query rows per workgroup (one per lane)
+constexpr int kF32Waves = 4;   // key-split waves per workgroup
+constexpr int kF32Keys = 16;   // keys per tile
 
 template <int DQK, int DV>
-__global__ void __launch_bounds__(kF32Rows) attn_step_f32_kernel(StepArgs a) {
-  __shared__ float Ks[kF32Keys][DQK];
-  __shared__ float Vs[kF32Keys][DV];
-  const int lane = threadIdx.x;
+struct F32Smem {
+  static constexpr int kTile = kF32Waves * kF32Keys * (DQK + DV);        // every wave's K and V tile
+  static constexpr int kMerge = (kF32Waves - 1) * (DV + 2) * kF32Rows;   // waves 1..3: O, max, sum
+  static constexpr int kFloats = kTile > kMerge ? kTile : kMerge;
+};
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(kF32Rows * kF32Waves) attn_step_f32_kernel(StepArgs a) {
+  __shared__ float smem[F32Smem<DQK, DV>::kFloats];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* const Ks = smem + wave * kF32Keys * (DQK + DV);   // [kF32Keys][DQK]
+  float* const Vs = Ks + kF32Keys * DQK;                    // [kF32Keys][DV]
   const int logical = xcd_contiguous_id(blockIdx.x, a.total_wgs);
   int qt = logical % a.n_qtiles;
   const int rest = logical / a.n_qtiles;
@@ -904,26 +919,33 @@ __global__ void __launch_bounds__(kF32Rows) attn_step_f32_kernel(StepArgs a) {
   for (int d = 0; d < DV; ++d) acc[d] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int64_t key0 = 0; key0 < nkeys; key0 += kF32Keys) {
-    __syncthreads();
-    for (int i = lane; i < kF32Keys * DQK; i += kF32Rows) {
-      const int64_t key = key0 + i / DQK;
-      Ks[i / DQK][i % DQK] =
-          key < a.sk ? kg[((static_cast<int64_t>(b) * a.sk + key) * a.hkv + kvh) * DQK + i % DQK] : 0.f;
+  // Every wave runs the same number of iterations (the barriers stay
+  // uniform); a wave past the last tile idles through its last one.
+  const int64_t ntiles = (nkeys + kF32Keys - 1) / kF32Keys;
+  const int64_t n_iter = (ntiles + kF32Waves - 1) / kF32Waves;
+  for (int64_t it = 0; it < n_iter; ++it) {
+    const int64_t key0 = (it * kF32Waves + wave) * kF32Keys;
+    const bool live = key0 < nkeys;
+    __syncthreads();   // this wave is done reading its previous tile
+    if (live) {
+      for (int i = lane; i < kF32Keys * DQK; i += kF32Rows) {
+        const int64_t key = key0 + i / DQK;
+        Ks[i] = key < a.sk ? kg[((static_cast<int64_t>(b) * a.sk + key) * a.hkv + kvh) * DQK + i % DQK] : 0.f;
+      }
+      for (int i = lane; i < kF32Keys * DV; i += kF32Rows) {
+        const int64_t key = key0 + i / DV;
+        Vs[i] = key < a.sk ? vg[((static_cast<int64_t>(b) * a.sk + key) * a.hkv + kvh) * DV + i % DV] : 0.f;
+      }
     }
-    for (int i = lane; i < kF32Keys * DV; i += kF32Rows) {
-      const int64_t key = key0 + i / DV;
-      Vs[i / DV][i % DV] =
-          key < a.sk ? vg[((static_cast<int64_t>(b) * a.sk + key) * a.hkv + kvh) * DV + i % DV] : 0.f;
-    }
     __syncthreads();
+    if (!live) continue;
     float s[kF32Keys];
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int d = 0; d < DQK; ++d) dot = fmaf(qr[d], Ks[j][d], dot);
+      for (int d = 0; d < DQK; ++d) dot = fmaf(qr[d], Ks[j * DQK + d], dot);
       const int64_t key = key0 + j;
       const bool vis = key < a.sk && (!a.causal || a.k_pos0 + key <= qpos);
       s[j] = vis ? dot : kNegInf;
@@ -944,11 +966,40 @@ __global__ void __launch_bounds__(kF32Rows) attn_step_f32_kernel(StepArgs a) {
     for (int d = 0; d < DV; ++d) {
       float x = acc[d] * alpha;
 #pragma unroll
-      for (int j = 0; j < kF32Keys; ++j) x = fmaf(s[j], Vs[j][d], x);
+      for (int j = 0; j < kF32Keys; ++j) x = fmaf(s[j], Vs[j * DV + d], x);
       acc[d] = x;
     }
   }
-  if (!row_valid) return;
+
+  // Merge the waves' states into wave 0 through LDS: [wave-1][DV + 2][lane].
+  __syncthreads();   // every wave is done with its tiles
+  if (wave > 0) {
+    float* mine = smem + (wave - 1) * (DV + 2) * kF32Rows + lane;
+#pragma unroll
+    for (int d = 0; d < DV; ++d) mine[d * kF32Rows] = acc[d];
+    mine[DV * kF32Rows] = m_run;
+    mine[(DV + 1) * kF32Rows] = l_run;
+  }
+  __syncthreads();
+  if (wave > 0 || !row_valid) return;
+  float m_all = m_run;
+#pragma unroll
+  for (int w = 1; w < kF32Waves; ++w) m_all = fmaxf(m_all, smem[((w - 1) * (DV + 2) + DV) * kF32Rows + lane]);
+  const float m_use = m_all == kNegInf ? 0.f : m_all;
+  const float f0 = exp2f((m_run - m_use) * a.scale_log2);   // 0 for a wave that saw no key
+  l_run *= f0;
+#pragma unroll
+  for (int d = 0; d < DV; ++d) acc[d] *= f0;
+#pragma unroll
+  for (int w = 1; w < kF32Waves; ++w) {
+    const float* theirs = smem + (w - 1) * (DV + 2) * kF32Rows + lane;
+    const float f = exp2f((theirs[DV * kF32Rows] - m_use) * a.scale_log2);
+    l_run += theirs[(DV + 1) * kF32Rows] * f;
+#pragma unroll
+    for (int d = 0; d < DV; ++d) acc[d] += theirs[d * kF32Rows] * f;
+  }
+  m_run = m_all;
+
   const bool has = m_run != kNegInf && l_run > 0.f;
   const float inv = has ? 1.f / l_run : 0.f;
   const float lse_blk = has ? m_run * a.scale + logf(l_run) : kNegInf;
@@ -1270,11 +1321,11 @@ extern "C" int32_t ring_attn_step(const void* q, const void* k, const void* v, i
         rc = launch_bf16_any(d_qk, ja, batch, st);
       } else {
         if (d_qk == 64)
-          rc = launch(attn_step_f32_kernel<64, 64>, kF32Rows, kF32Rows, args, batch, st);
+          rc = launch(attn_step_f32_kernel<64, 64>, kF32Rows, kF32Rows * kF32Waves, args, batch, st);
         else if (d_qk == 128)
-          rc = launch(attn_step_f32_kernel<128, 128>, kF32Rows, kF32Rows, args, batch, st);
+          rc = launch(attn_step_f32_kernel<128, 128>, kF32Rows, kF32Rows * kF32Waves, args, batch, st);
         else
-          rc = launch(attn_step_f32_kernel<192, 128>, kF32Rows, kF32Rows, args, batch, st);
+          rc = launch(attn_step_f32_kernel<192, 128>, kF32Rows, kF32Rows * kF32Waves, args, batch, st);
       }
       if (rc != CP_OK) return rc;
     }
