@@ -54,3 +54,39 @@ def compare(o, lse, o_ref, lse_ref, o_tol, lse_tol, what=""):
     if nrm > 0:
         assert rel <= REL_L2, f"{what}: relative L2 error {rel} > {REL_L2}"
     return err_o, err_l, rel
+
+
+def whole_output_properties(o, lse, q, k, v, q_pos, k_pos0, group, scale, what):
+    """Properties every row of a causal attention output must have, checked
+    on the device over all rows (the sampled rows are checked exactly):
+
+    * O and LSE are finite (every row sees at least one key);
+    * O is a convex combination of the visible V rows, so each element lies
+      within the column range of its kv head's V;
+    * LSE = ln sum exp(s) is at least the score of any visible key: key 0 and
+      the row's own position are visible to every row here;
+    * LSE is at most the largest possible score (|q| max|k| scale) plus the
+      log of the number of keys the row sees.
+
+    o [S, H, dv] / lse [S, H] float32; q [S, H, d], k / v [Sk, Hkv, d] bf16 at
+    absolute positions q_pos (device int64 [S]) and k_pos0 + arange(Sk)."""
+    import torch
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all(), f"{what}: non-finite output"
+    hkv = k.shape[1]
+    vmin = v.float().amin(0).repeat_interleave(group, 0)          # [H, dv]
+    vmax = v.float().amax(0).repeat_interleave(group, 0)
+    slack = 1e-3
+    assert bool((o >= vmin - slack).all()) and bool((o <= vmax + slack).all()), \
+        f"{what}: O outside the range of V"
+    for key_idx in (torch.zeros_like(q_pos), q_pos - k_pos0):
+        kk = k[key_idx].float().repeat_interleave(group, 1)       # [S, H, d]
+        chunk = 8192
+        for a0 in range(0, q.shape[0], chunk):
+            s_ = (q[a0:a0 + chunk].float() * kk[a0:a0 + chunk]).sum(-1) * scale
+            assert bool((lse[a0:a0 + chunk] >= s_ - 1e-3).all()), f"{what}: LSE below a visible score"
+        del kk
+    qn = q.float().norm(dim=-1)                                   # [S, H]
+    kmax = k.float().norm(dim=-1).amax(0).repeat_interleave(group, 0)   # [H]
+    n_vis = (q_pos - k_pos0 + 1).double().log().float()[:, None]
+    assert bool((lse <= qn * kmax * scale + n_vis + 1e-3).all()), f"{what}: LSE above its bound"
+    say(f"  {what}: all {o.shape[0] * o.shape[1]} rows finite, within V's range and the LSE bounds")

@@ -12,13 +12,17 @@ visible to it, so the oracle evaluated on those rows is exact for them.
       Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
       few tokens.
   C5  segmented chunked prefill (MLA shape): 544 (token, head) rows.
+C4 and C5 are also checked over every row, on the device, for properties any
+correct output has (finite; inside the range of its kv head's V; LSE between
+the score of a key every row sees and the largest possible score plus the
+log of the number of keys seen).
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import host64, compare, say, tensor, F32_O, BF16_O, BF16_LSE
+from gpu_util import host64, compare, say, tensor, whole_output_properties, F32_O, BF16_O, BF16_LSE
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -140,6 +144,9 @@ def test_c4_long_zigzag_sampled(ra):
     k_full, v_full = w["k_full"], w["v_full"]
     _sampled_rows_check(o, lse, q_rows, lambda g: host64(k_full[0, :, g]),
                         lambda g: host64(v_full[0, :, g]), q_pos, hh, hq // hkv, "C4")
+    qp = torch.as_tensor(np.asarray(w["local"]), device="cuda")
+    whole_output_properties(w["o"][0], w["lse"][0], w["q_local"][0], k_full[0], v_full[0], qp, 0,
+                             hq // hkv, 1.0 / np.sqrt(w["d"]), "C4")
     del w, k_full, v_full
     _release()
 
@@ -170,6 +177,9 @@ def test_c5_segmented_sampled(ra):
     k, v = w["k"], w["v"]
     _sampled_rows_check(o, lse, q_rows, lambda g: host64(k[0, :, g]), lambda g: host64(v[0, :, g]),
                         q_pos, hh, 1, "C5")
+    qp = w["q_pos0"] + torch.arange(sq, device="cuda")
+    whole_output_properties(w["o"][0], w["lse"][0], w["q"][0], k[0], v[0], qp, 0, 1,
+                             1.0 / np.sqrt(w["dqk"]), "C5")
     del w, k, v
     _release()
 
