@@ -270,8 +270,11 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   constexpr int kStageElems = SPLIT * 2 * (C::KTILE + C::VTILE);
   constexpr int kSwapElems = SPLIT == 2 ? 8 * (16 * (C::DB / 2) + 2) * 64 * 2 : 0;   // floats as uint16 pairs
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStageElems > kSwapElems ? kStageElems : kSwapElems];
-  uint16_t* const Ks = smem;
-  uint16_t* const Vs = smem + SPLIT * 2 * C::KTILE;
+  // (d_qk = 192: V stages first, so the transposed V reads keep their whole
+  // offset in the 16-bit immediate; only K stage 1's second half reaches past
+  // 64 KB)
+  uint16_t* const Ks = smem + (DQK > 128 ? SPLIT * 2 * C::VTILE : 0);
+  uint16_t* const Vs = smem + (DQK > 128 ? 0 : SPLIT * 2 * C::KTILE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
