@@ -7,6 +7,10 @@
   256-row workgroups (sampled heads).
 * lse_merge at its largest head dimension (512) over 16 parts, and at the
   smallest (4) with bf16 output.
+* One K/V segment of more than a million keys (2 GiB per tensor): the tile
+  descriptors are re-based every 2^30 bytes, and with a ragged end every tile
+  gets its own descriptor at offsets past 2^31, in the 8-wave, the 8-wave
+  with backward (odd-round) sweeps and the 256-row forms (sampled rows).
 
 Every result is compared element by element with the oracle."""
 
@@ -104,3 +108,45 @@ def test_lse_merge_at_its_head_dim_limits(ra, n, rows, dv, out_bf16):
         # bf16 output: round-to-nearest-even leaves at most half an ulp, i.e.
         # 2^-8 of the value, on top of the float32 merge
         assert np.all(np.abs(o_gpu - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + 1e-5)
+
+
+# (sk, sq, hq): queries at the end of the sequence see every key (causal)
+HUGE = [
+    (1 << 20, 64, 8),            # whole tiles: 8-wave, one round
+    ((1 << 20) + 37, 64, 8),     # ragged end: a descriptor per tile, offsets past 2^31
+    ((1 << 20) + 37, 640, 64),   # 8-wave, 320 workgroups: odd rounds sweep backwards
+    (1 << 20, 1024, 128),        # 256-row workgroups (512 of them)
+]
+
+
+@pytest.mark.parametrize("idx", range(len(HUGE)))
+def test_segment_of_more_than_2_gib(ra, idx):
+    import seeded_inputs as si
+    sk, sq, hq = HUGE[idx]
+    hkv, d = 8, 128
+    say(f"huge segment case {idx}: sk={sk} sq={sq} hq={hq} hkv={hkv} d={d}")
+    k = si.device_normal(600, 2, idx, (1, sk, hkv, d), torch.bfloat16, "cuda")
+    v = si.device_normal(600, 3, idx, (1, sk, hkv, d), torch.bfloat16, "cuda")
+    q = si.device_normal(600, 1, idx, (1, sq, hq, d), torch.bfloat16, "cuda")
+    q0 = sk - sq
+    o = torch.empty((1, sq, hq, d), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    ra.ring_attn_step(q, k, v, o, lse, q_pos0=q0, k_pos0=0, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    group = hq // hkv
+    rows = [(t, h) for t in sorted({0, 1, sq // 2, sq - 1}) for h in sorted({0, hq - 1, hq // 2 + 1})]
+    for kvh in sorted({h // group for _, h in rows}):
+        sel = [(t, h) for t, h in rows if h // group == kvh]
+        tt = np.array([t for t, _ in sel])
+        hh = np.array([h for _, h in sel])
+        k64, v64 = host64(k[0, :, kvh]), host64(v[0, :, kvh])
+        q64 = host64(q[0][torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()])
+        ro, rl = oracle.attention_ref(q64[None, :, None, :], k64[None, :, None, :], v64[None, :, None, :],
+                                      q0 + tt, np.arange(sk), causal=True)
+        o_s = host64(o[0][torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()])
+        l_s = host64(lse[0][torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()])
+        compare(o_s, l_s, ro[0, :, 0], rl[0, :, 0], BF16_O, BF16_LSE, f"huge {idx} kv head {kvh}")
+        del k64, v64
+    del k, v, q, o, lse
+    torch.cuda.empty_cache()
