@@ -12,6 +12,8 @@ visible to it, so the oracle evaluated on those rows is exact for them.
       Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
       few tokens.
   C5  segmented chunked prefill (MLA shape): 544 (token, head) rows.
+The standalone merge (2 x 8,388,608 rows x 128) and the reorganisation
+gather (135,168 K and V rows) are checked at the sizes the bench times.
 C4 and C5 are also checked over every row, on the device, for properties any
 correct output has (finite; inside the range of its kv head's V; LSE between
 the score of a key every row sees and the largest possible score plus the
@@ -209,4 +211,59 @@ def test_large_grid_ragged_sampled(ra, dqk, dv, hq, hkv):
                         lambda g: host64(k[0, :, g]), lambda g: host64(v[0, :, g]), q0 + tt, hh,
                         hq // hkv, "large grid")
     del q, k, v, o, lse
+    _release()
+
+
+def test_lse_merge_at_the_benched_size(ra):
+    """The standalone merge as benched: 2 partials of the 1M-token share's
+    8,388,608 rows x 128 (8.6 GB in).  Sampled rows (the first, the last and
+    seeded random ones) against the oracle, every row finite."""
+    import seeded_inputs as si
+    rows, dv, n = 131072 * 64, 128, 2
+    o_parts = si.device_normal(7, 1, 0, (n, rows, dv), torch.float32, "cuda")
+    lse_parts = si.device_normal(7, 2, 0, (n, rows), torch.float32, "cuda") * 3
+    lse_parts[1, rows - 5:] = float("-inf")             # the last rows: one part empty
+    o_parts[1, rows - 5:] = 0.0
+    o, lse = ra.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(8)
+    pick = np.unique(np.concatenate([[0, 1, rows // 2, rows - 6, rows - 5, rows - 1],
+                                     rng.integers(0, rows, 2000)]))
+    idx = torch.from_numpy(pick).cuda()
+    op, lp = host64(o_parts[:, idx]), host64(lse_parts[:, idx])
+    o_ref, lse_ref = oracle.lse_merge_ref(list(op), list(lp))
+    compare(host64(o[idx]), host64(lse[idx]), o_ref, lse_ref, 1e-5, 1e-5,
+            f"merge of 2 x {rows} rows ({len(pick)} sampled)")
+    del o_parts, lse_parts, o, lse
+    _release()
+
+
+def test_reorg_gather_at_the_benched_size(ra):
+    """The all-gather-KV reorganisation as benched (135,168 tokens of 4
+    requests on 8 devices, K 128 x 192 and V 128 x 128 bf16): the row index
+    bit for bit against the oracle, and the gathered K and V rows, all of
+    them, equal to the source rows the index names (compared on the device,
+    byte for byte)."""
+    import workloads
+    w = workloads.reorg_setup()
+    src_ref, _ = oracle.reorg_index_ref(w["lens"], 128, 16, 1, 8)
+    assert np.array_equal(w["idx"].cpu().numpy(), src_ref)
+    ok = ra.gather_rows(w["gk"], w["idx"])
+    ov = ra.gather_rows(w["gv"], w["idx"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    pick = np.unique(np.concatenate([[0, 1, w["n"] - 1], rng.integers(0, w["n"], 2000)]))
+    for got, src, name in ((ok, w["gk"], "K"), (ov, w["gv"], "V")):
+        # sampled rows on the host, against the oracle's index
+        g = got[torch.from_numpy(pick).cuda()].view(torch.int16).cpu().numpy()
+        e = src[torch.from_numpy(src_ref[pick]).cuda()].view(torch.int16).cpu().numpy()
+        assert np.array_equal(g, e), f"{name}: sampled rows differ"
+        # every row: dst[i] is src[idx[i]] (the definition), byte for byte on the device
+        ref_idx = torch.from_numpy(src_ref).cuda()
+        for a0 in range(0, w["n"], 16384):
+            exp = src.view(torch.int16)[ref_idx[a0:a0 + 16384]]
+            assert torch.equal(got.view(torch.int16)[a0:a0 + 16384], exp), f"{name} rows {a0}.."
+    say(f"  reorg gather: {w['n']} K and V rows equal to their source rows")
+    del w, ok, ov
     _release()
