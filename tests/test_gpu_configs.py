@@ -12,8 +12,9 @@ visible to it, so the oracle evaluated on those rows is exact for them.
       Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
       few tokens.
   C5  segmented chunked prefill (MLA shape): 544 (token, head) rows.
-The standalone merge (2 x 8,388,608 rows x 128) and the reorganisation
-gather (135,168 K and V rows) are checked at the sizes the bench times.
+The standalone merge (2 x 8,388,608 rows x 128), the reorganisation gather
+(135,168 K and V rows) and the packed 16-request prefill (69,952 tokens) are
+checked at the sizes the bench times.
 C4 and C5 are also checked over every row, on the device, for properties any
 correct output has (finite; inside the range of its kv head's V; LSE between
 the score of a key every row sees and the largest possible score plus the
@@ -266,4 +267,36 @@ def test_reorg_gather_at_the_benched_size(ra):
             assert torch.equal(got.view(torch.int16)[a0:a0 + 16384], exp), f"{name} rows {a0}.."
     say(f"  reorg gather: {w['n']} K and V rows equal to their source rows")
     del w, ok, ov
+    _release()
+
+
+def test_varlen_at_the_benched_size(ra):
+    """The packed 16-request prefill as benched (lengths 512..8192, 69,952
+    tokens, self-causal, GQA 32/8, d 128): per request, sampled rows against
+    the oracle and every row checked for the whole-output properties."""
+    import workloads
+    w = workloads.varlen_setup()
+    ra.ring_attn_step_varlen(w["q"], w["k"], w["v"], w["cu"], w["cu"], w["pos"], w["pos"],
+                             o=w["o"], lse=w["lse"], causal=True)
+    torch.cuda.synchronize()
+    hq, hkv, d = w["hq"], w["hkv"], w["d"]
+    group, scale = hq // hkv, 1.0 / np.sqrt(d)
+    rng = np.random.default_rng(12)
+    for r, L in enumerate(w["lens"]):
+        a0, L = int(w["cu"][r]), int(L)
+        sl = slice(a0, a0 + L)
+        whole_output_properties(w["o"][sl], w["lse"][sl], w["q"][sl], w["k"][sl], w["v"][sl],
+                                torch.arange(L, device="cuda"), 0, group, scale, f"varlen request {r}")
+        toks = np.unique(np.array([0, 1, 63, 64, L // 2, L - 1] + rng.integers(0, L, 4).tolist()))
+        heads = np.array([0, hq - 1, int(rng.integers(0, hq))])
+        for h in np.unique(heads):
+            kvh = int(h) // group
+            k64, v64 = host64(w["k"][sl, kvh]), host64(w["v"][sl, kvh])
+            ti = torch.from_numpy(a0 + toks).cuda()
+            q64 = host64(w["q"][ti, int(h)])
+            ro, rl = oracle.attention_ref(q64[None, :, None, :], k64[None, :, None, :], v64[None, :, None, :],
+                                          toks, np.arange(L), causal=True)
+            compare(host64(w["o"][ti, int(h)]), host64(w["lse"][ti, int(h)]), ro[0, :, 0], rl[0, :, 0],
+                    BF16_O, BF16_LSE, f"varlen request {r} (L={L}) head {h}")
+    del w
     _release()
