@@ -622,6 +622,38 @@ def context_bench():
                               "what": "1 GiB device-to-device tensor copy, read + write bytes"}}
 
 
+def host_index_bench():
+    """The host-side index calls at the workloads' sizes, as tokens per second
+    (they run on the host, with no device roofline): the head-tail partition
+    of the 1M-token sequence for every rank of cp 8, the slot mapping of the
+    decode workload's 64 x 131,072 positions over 8 devices, and the
+    reorganisation index of the 135,168-token all-gathered context (4
+    requests, 8 devices).  Each is the median of 5 calls through the
+    binding (ctypes and numpy allocation included), on one host thread."""
+    import ring_attention_02_amd as ra
+
+    def med(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    seq, cp = 1 << 20, 8
+    t_part = med(lambda: [ra.partition([seq], cp, r) for r in range(cp)])
+    pos = np.arange(131072, dtype=np.int64)
+    t_slot = med(lambda: [ra.slot_mapping(pos, 128, 16, 8, 1) for _ in range(64)])
+    lens = [50000, 40000, 30000, 15168]
+    t_reorg = med(lambda: ra.reorg_index(lens, 128, 16, 1, 8))
+    return {"cp_partition": {"value": round(cp * seq / t_part / 1e6, 2), "unit": "M tokens/s",
+                             "what": "1,048,576 tokens, cp 8, all 8 ranks (local list + restore index)"},
+            "cp_slot_mapping": {"value": round(64 * 131072 / t_slot / 1e6, 2), "unit": "M tokens/s",
+                                "what": "64 requests x 131,072 positions, block 128, interleave 16, 8 devices"},
+            "cp_reorg_index": {"value": round(sum(lens) / t_reorg / 1e6, 2), "unit": "M tokens/s",
+                               "what": "135,168 tokens of 4 requests on 8 devices, block 128, interleave 16"}}
+
+
 def long_step_only(reps):
     """One FULL ring step of the 1M-token zigzag prefill (rank 0, cp 8): the
     launch that attends the tail query part to a whole staged block and
@@ -979,6 +1011,9 @@ def main():
                 "roofline": roofline_entry("hbm", b6 / s6 / 1e9, PEAK_HBM_GBS, "GB/s",
                                            profiled_traffic("lse_merge_2x8M.md", "lse_merge.hip"))}
         out["secondary"] = sec
+        if not only or "host" in only:
+            log("host index calls: partition, slot mapping, reorganisation index")
+            out["host_index"] = host_index_bench()
         if not only or "context" in only:
             log("context: vendor bf16 GEMM and a plain device copy on the same GPU")
             out["context"] = context_bench()

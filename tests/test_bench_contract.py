@@ -74,3 +74,14 @@ def test_roofline_entry_shape():
     assert e == {"bound": "mfma", "achieved": 500.0, "peak": 2500.0, "unit": "TFLOP/s",
                  "frac": 0.2, "traffic": 123}
     json.dumps(e)
+
+
+def test_host_index_leg_reports_tokens_per_second():
+    # the index calls run on the host, so this leg runs without a GPU too
+    sys.path.insert(0, ROOT)
+    import bench
+    r = bench.host_index_bench()
+    assert set(r) == {"cp_partition", "cp_slot_mapping", "cp_reorg_index"}
+    for v in r.values():
+        assert v["unit"] == "M tokens/s" and v["value"] > 0
+    json.dumps(r)
