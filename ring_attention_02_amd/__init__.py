@@ -55,11 +55,11 @@ _lib.cp_partition.argtypes = [_vp, _i32, _i32, _i32, _vp, _pi64, _vp, _pi64]
 _lib.cp_slot_mapping.restype = _i32
 _lib.cp_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp]
 _lib.cp_classify.restype = _i32
+_lib.cp_classify.argtypes = [_i64, _i64, _i64, _i64, _i32, _pi32]
 _lib.cp_reorg_index.restype = _i32
 _lib.cp_reorg_index.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _pi64, _vp, _i64]
 _lib.cp_ring_schedule.restype = _i32
 _lib.cp_ring_schedule.argtypes = [_i32, _i32, _vp, _vp]
-_lib.cp_classify.argtypes = [_i64, _i64, _i64, _i64, _i32, _pi32]
 _lib.ring_attn_step.restype = _i32
 _lib.ring_attn_step.argtypes = [_vp, _vp, _vp, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
                                 _i64, _i64, _i32, _f32, _i32, _vp, _vp, _pi32, _vp]
