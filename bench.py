@@ -430,12 +430,22 @@ def short_zigzag_bench(sweeps=50, warmup=20):
     t_compute = graph_ms(compute, sweeps)
     copies = [lambda u=u: ra.stage_copy(ring.forward_pairs(u)) for u in range(1, ring.cp)]
     t_copy = graph_ms(copies, sweeps)
+    # every rank of the ring, the same way (50 sweeps as one graph): the
+    # zigzag partition gives each the same visible pairs, in other step shapes
+    per_rank = []
+    for r in range(ring.cp):
+        wr = w if r == w["rank"] else workloads.zigzag_setup(2, rank=r)
+        g = wr["ring"].capture(wr["q_local"], wr["o"], wr["lse"], sweeps=sweeps)
+        graph_upload(g)
+        wr["ring"].run(wr["q_local"], wr["o"], wr["lse"])
+        per_rank.append(time_steps(g.replay, 1, 1) / sweeps * 1e3)
+        del g, wr
     flops_per_launch = w["flops"] / len(launches)
     return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=len(launches),
                         achieved_tflops=flops_per_launch / (mean_ms * 1e-3) / 1e12,
                         full_ms=full_ms, diag_ms=diag_ms, eager_ms=eager * 1e3,
                         side_ms=side * 1e3, per_graph_ms=per_graph * 1e3,
-                        t_sweep_ms=t_sweep, t_compute_ms=t_compute, t_copy_ms=t_copy,
+                        t_sweep_ms=t_sweep, t_compute_ms=t_compute, t_copy_ms=t_copy, per_rank_ms=per_rank,
                         overlap=(t_compute + t_copy - t_sweep) / t_copy)
 
 
@@ -921,6 +931,7 @@ def main():
                 "diag_step_ms": round(l2["diag_ms"], 5),
                 "one_graph_per_sweep_ms": round(l2["per_graph_ms"], 4), "eager_ms": round(l2["eager_ms"], 4),
                 "side_stream_copies_ms": round(l2["side_ms"], 4),
+                "per_rank_sweep_ms": [round(x, 4) for x in l2["per_rank_ms"]],
                 "overlap": {"efficiency": round(l2["overlap"], 3), "t_sweep_ms": round(l2["t_sweep_ms"], 4),
                             "t_compute_only_ms": round(l2["t_compute_ms"], 4),
                             "t_copies_only_ms": round(l2["t_copy_ms"], 4),

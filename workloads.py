@@ -47,12 +47,14 @@ def causal_pairs(q_pos0, sq, k_pos0, sk):
     return total
 
 
-def zigzag_setup(cfg_id):
-    """C2 / C4: rank 0's local Q, every rank's K/V, the ring and its FLOP count."""
+def zigzag_setup(cfg_id, rank=None):
+    """C2 / C4: a rank's local Q (the workload's rank 0 unless another is
+    named), every rank's K/V, the ring and its FLOP count."""
     import ring_attention_02_amd as ra
     torch = _torch()
     c = CONFIGS[cfg_id]
-    seq, cp, rank, hq, hkv, d = c["seq"], c["cp"], c["rank"], c["hq"], c["hkv"], c["d"]
+    seq, cp, hq, hkv, d = c["seq"], c["cp"], c["hq"], c["hkv"], c["d"]
+    rank = c["rank"] if rank is None else rank
     parts = 2 * cp
     chunk = seq // parts
     big = cfg_id == 4
