@@ -384,8 +384,21 @@ def long_headline(steps, warmup):
     # (ring_stage_copy launches, one HIP graph), against the sweep.
     copies = [lambda u=u: ra.stage_copy(ring.forward_pairs(u)) for u in range(1, ring.cp)]
     t_copy_ms = graph_ms(copies, 1, 3)
+    # one sweep of every other rank's share (same K/V, its own Q parts and
+    # ring order), timed like the headline's: the zigzag partition gives
+    # every rank the same visible pairs in other step shapes
+    per_rank = [sec * 1e3]
+    for r in range(1, ring.cp):
+        wr = workloads.zigzag_setup(4, rank=r)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        wr["ring"].run(wr["q_local"], wr["o"], wr["lse"])
+        torch.cuda.synchronize()
+        per_rank.append((time.perf_counter() - t0) * 1e3)
+        del wr
+        torch.cuda.empty_cache()
     return w, sec, dict(mean_launch_ms=mean_ms, launches_per_step=launches,
-                        flops_per_launch=flops_per_launch, t_copy_ms=t_copy_ms,
+                        flops_per_launch=flops_per_launch, t_copy_ms=t_copy_ms, per_rank_ms=per_rank,
                         achieved_tflops=flops_per_launch / (mean_ms * 1e-3) / 1e12,
                         full_ms=full_ms, diag_ms=float(np.mean(diag)) if diag else None)
 
@@ -901,6 +914,7 @@ def main():
                    "timing": "HIP events around every launch of the timed sweeps, on the launch stream"},
         "launch": {"mode": "one ring_attn_step_jobs launch per ring step, issued eagerly; each launch "
                            "also copies the next K/V block into the idle staging slot",
+                   "per_rank_sweep_ms": [round(x, 1) for x in l4["per_rank_ms"]],
                    "forwarded_blocks_alone_ms": round(l4["t_copy_ms"], 3),
                    "forwarded_share_of_sweep": round(l4["t_copy_ms"] / (sec4 * 1e3), 5),
                    "full_step_traffic_bytes": profiled_traffic(
