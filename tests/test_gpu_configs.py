@@ -8,14 +8,15 @@ visible to it, so the oracle evaluated on those rows is exact for them.
       the restore index bit for bit.
   C3  GQA decode over 8 shards, 64 x 131072: per-shard partials and merged
       output of 3 whole requests (all heads).
-  C4  zigzag rank 0 of 1M tokens, cp 8: 640 (token, head) rows covering both
+  C4  zigzag rank 0 of 1M tokens, cp 8: 512 (token, head) rows covering both
       Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
-      few tokens.
-  C5  segmented chunked prefill (MLA shape): 544 (token, head) rows.
+      few tokens; rank 7 of the same ring (both query parts busy at every
+      step): 162 rows.
+  C5  segmented chunked prefill (MLA shape): 541 (token, head) rows.
 The standalone merge (2 x 8,388,608 rows x 128), the reorganisation gather
 (135,168 K and V rows) and the packed 16-request prefill (69,952 tokens) are
 checked at the sizes the bench times.
-C4 and C5 are also checked over every row, on the device, for properties any
+C4 (ranks 0 and 7) and C5 are also checked over every row, on the device, for properties any
 correct output has (finite; inside the range of its kv head's V; LSE between
 the score of a key every row sees and the largest possible score plus the
 log of the number of keys seen).
@@ -150,6 +151,38 @@ def test_c4_long_zigzag_sampled(ra):
     qp = torch.as_tensor(np.asarray(w["local"]), device="cuda")
     whole_output_properties(w["o"][0], w["lse"][0], w["q_local"][0], k_full[0], v_full[0], qp, 0,
                              hq // hkv, 1.0 / np.sqrt(w["d"]), "C4")
+    del w, k_full, v_full
+    _release()
+
+
+def test_c4_last_rank_sampled(ra):
+    """Rank 7 of the same 1M-token ring: its head part (chunk 7) sees a part
+    of every block it receives and its tail part (chunk 8) only the head
+    chunks, so every step runs both query parts (rank 0's head part is done
+    after step 0).  Sampled rows against the oracle, every row checked for
+    the whole-output properties."""
+    import workloads
+    w = workloads.zigzag_setup(4, rank=7)
+    w["ring"].run(w["q_local"], w["o"], w["lse"])
+    torch.cuda.synchronize()
+    c, hq, hkv = w["chunk"], w["hq"], w["hkv"]
+    n_local = w["q_local"].shape[1]
+    rng = np.random.default_rng(47)
+    toks = {0, 1, 64, c - 1, c, c + 1, 2 * c - 1} | set(rng.integers(0, n_local, 20).tolist())
+    rows = sorted({(t, int(h)) for t in toks for h in rng.choice(hq, 6, replace=False)})
+    tt = np.array([r[0] for r in rows])
+    hh = np.array([r[1] for r in rows])
+    ti, hi = torch.from_numpy(tt).cuda(), torch.from_numpy(hh).cuda()
+    o, lse = host64(w["o"][0][ti, hi]), host64(w["lse"][0][ti, hi])
+    q_rows = host64(w["q_local"][0][ti, hi])
+    q_pos = np.asarray(w["local"])[tt]
+    say(f"C4 rank 7: {len(rows)} sampled rows")
+    k_full, v_full = w["k_full"], w["v_full"]
+    _sampled_rows_check(o, lse, q_rows, lambda g: host64(k_full[0, :, g]),
+                        lambda g: host64(v_full[0, :, g]), q_pos, hh, hq // hkv, "C4 rank 7")
+    qp = torch.as_tensor(np.asarray(w["local"]), device="cuda")
+    whole_output_properties(w["o"][0], w["lse"][0], w["q_local"][0], k_full[0], v_full[0], qp, 0,
+                            hq // hkv, 1.0 / np.sqrt(w["d"]), "C4 rank 7")
     del w, k_full, v_full
     _release()
 
