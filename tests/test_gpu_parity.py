@@ -380,6 +380,30 @@ def test_peaked_scores_exercise_max_raises(ra, causal):
     compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "peaked")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jump_beyond_the_exp2_range(ra, causal):
+    """Keys planted equal to a query (queries scaled x8) late in the block:
+    their scores exceed every earlier score of the row by about 1000 in log2
+    units, so exponentials taken against the earlier running max would
+    overflow float32; the result must still match the oracle."""
+    sq, sk, hq, hkv, d = 130, 700, 2, 1, 128
+    q, _ = tensor(62, 1, 0, (1, sq, hq, d), torch.float32)
+    k, _ = tensor(62, 2, 0, (1, sk, hkv, d), torch.float32)
+    v, _ = tensor(62, 3, 0, (1, sk, hkv, d), torch.bfloat16)
+    q = q * 8.0
+    k[0, 650, 0] = q[0, 100, 0]                    # row 100 of head 0: score |q|^2
+    k[0, 690:700, 0] = q[0, 120:130, 1] * 1.5      # rows 120..129 of head 1, later still
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o = torch.empty((1, sq, hq, d), device="cuda")
+    lse = torch.empty((1, sq, hq), device="cuda")
+    ra.ring_attn_step(qb, kb, v, o, lse, q_pos0=600, k_pos0=0, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(host64(qb), host64(kb), host64(v), 600 + np.arange(sq),
+                                          np.arange(sk), causal)
+    assert lse_ref[0, 100, 0] > 600.0          # the planted score (natural-log units) dominates its row
+    compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "score jump")
+
+
 def test_stage_copy_pieces(ra):
     src = [torch.randn(n, device="cuda") for n in (4096, 4, 100000 * 4, 12)]
     dst = [torch.full_like(x, -1.0) for x in src]
