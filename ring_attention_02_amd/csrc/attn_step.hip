@@ -123,6 +123,8 @@ struct VarlenArgs {
   JobArgs base;
   ReqDesc req[kMaxReq];
   int32_t n_req;
+  // causal launches: request r's workgroups are [wg_start[r], wg_start[r+1])
+  int32_t wg_start[kMaxReq + 1];
 };
 template <bool VARLEN>
 struct KernelArgs {
@@ -314,19 +316,23 @@ attn_step_bf16_kernel(typename KernelArgs<VARLEN>::type args) {
   } else if constexpr (VARLEN) {
     // (jb0 names the request here)
     if (a.reverse_q) {
-      // Causal requests: the longest query tiles first across the whole grid
-      // (tile index outermost, descending; a tile's load grows with its
-      // index), then request, then query head within its kv group, kv head
-      // fastest.  Consecutive ids go to consecutive XCDs, so every XCD gets
-      // the same spread of tile lengths, longest first, and with 8 kv heads
-      // keeps to one of them (its q-heads share the XCD's L2).
-      int r = static_cast<int>(blockIdx.x);
-      const int kv = r % a.hkv;
-      r /= a.hkv;
-      const int gq = r % a.group;
-      r /= a.group;
-      jb0 = r % args.n_req;
-      qt0 = a.n_qtiles - 1 - r / args.n_req;
+      // Causal requests, request by request (the host orders them longest
+      // first), each request's query tiles longest first (a tile's load
+      // grows with its index), then the query head within its kv group, kv
+      // head fastest.  Consecutive ids go to consecutive XCDs, so with 8 kv
+      // heads each XCD keeps to one of them, and the workgroups it runs
+      // together are neighbouring tiles of one request: they sweep the same
+      // keys and share the XCD's L2.
+      const int id = static_cast<int>(blockIdx.x);
+      int r = 0;
+      while (r + 1 < args.n_req && args.wg_start[r + 1] <= id) ++r;
+      int local = id - args.wg_start[r];
+      const int kv = local % a.hkv;
+      local /= a.hkv;
+      const int gq = local % a.group;
+      local /= a.group;
+      jb0 = r;
+      qt0 = (args.req[r].q_len + BM - 1) / BM - 1 - local;
       rest = kv * a.group + gq;   // the query head (packed requests: batch 0)
     } else {
       // query tile fastest, then request
@@ -1194,7 +1200,18 @@ int32_t launch_bf16(JobArgs args, int64_t batch, hipStream_t stream) {
 template <int DQK, int DV, bool TAILS>
 int32_t launch_bf16_varlen_t(VarlenArgs args, int64_t max_q, hipStream_t stream) {
   const int64_t n_qtiles = (max_q + kBM - 1) / kBM;
-  const int64_t total = n_qtiles * args.n_req * args.base.hq;
+  int64_t total = n_qtiles * args.n_req * args.base.hq;
+  if (args.base.reverse_q) {   // request-major grid: each request's own tiles
+    int64_t acc = 0;
+    for (int r = 0; r < args.n_req; ++r) {
+      RA_CHECK(acc < (int64_t{1} << 31), CP_EUNSUPPORTED, "ring_attn_step_varlen: grid too large");
+      args.wg_start[r] = static_cast<int32_t>(acc);
+      acc += (static_cast<int64_t>(args.req[r].q_len) + kBM - 1) / kBM * args.base.hq;
+    }
+    RA_CHECK(acc < (int64_t{1} << 31), CP_EUNSUPPORTED, "ring_attn_step_varlen: grid too large");
+    args.wg_start[args.n_req] = static_cast<int32_t>(acc);
+    total = acc;
+  }
   RA_CHECK(total < (int64_t{1} << 31), CP_EUNSUPPORTED,
            "ring_attn_step_varlen: %lld workgroups exceed the grid limit", static_cast<long long>(total));
   if (total == 0) return CP_OK;
@@ -1552,8 +1569,15 @@ extern "C" int32_t ring_attn_step_varlen(const void* q, const void* k, const voi
     ja.scale = scale; ja.scale_log2 = scale * kLog2e;
     int64_t group_max_q = 0;
     const int32_t n = std::min(kMaxReq, n_req - r0);
+    // causal launches take the longest requests first
+    int32_t order[kMaxReq];
+    for (int32_t i = 0; i < n; ++i) order[i] = r0 + i;
+    if (ja.causal)
+      std::stable_sort(order, order + n, [&](int32_t x, int32_t y) {
+        return cu_seqlens_q[x + 1] - cu_seqlens_q[x] > cu_seqlens_q[y + 1] - cu_seqlens_q[y];
+      });
     for (int32_t i = 0; i < n; ++i) {
-      const int32_t r = r0 + i;
+      const int32_t r = order[i];
       ReqDesc& d = va.req[i];
       d.q_start = static_cast<int32_t>(cu_seqlens_q[r]);
       d.q_len = static_cast<int32_t>(cu_seqlens_q[r + 1] - cu_seqlens_q[r]);
