@@ -8,8 +8,10 @@
 // With M = max_k LSE_k:  LSE = M + ln sum_k exp(LSE_k - M),
 //                        O   = sum_k exp(LSE_k - LSE) * O_k.
 //
-// HBM-bound: every thread owns 16 (or 4) consecutive floats of one row; a
-// row's threads are adjacent, so each part is read with coalesced 16-B loads.
+// HBM-bound: a row's threads are adjacent and each owns four 16-B pieces of
+// it, tpr pieces apart (tpr = threads per row), so every load and store
+// instruction of a wave covers whole 128-B lines; parts are read and the
+// result written non-temporally (each byte is touched once).
 #include <hip/hip_runtime.h>
 
 #include "kernels_common.h"
@@ -21,8 +23,9 @@ namespace {
 constexpr int kMergeThreads = 256;
 
 // One pass over the parts with a running maximum (the same online rule the
-// attention kernels use): each thread owns UNROLL x 4 consecutive floats of
-// one row, so UNROLL independent 16-B loads per part are in flight.
+// attention kernels use): each thread owns UNROLL 16-B pieces of one row,
+// columns 4c + 4 tpr u, so UNROLL independent 16-B loads per part are in
+// flight and the tpr threads of a row write whole lines per instruction.
 template <bool OUT_BF16, int UNROLL>
 __global__ void __launch_bounds__(kMergeThreads)
 lse_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
@@ -42,10 +45,11 @@ lse_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ ls
   float m = kNegInf, tot = 0.f;
   for (int k = 0; k < n; ++k) {
     const float l = lse_parts[k * rows + row];
-    const float* src = o_parts + (k * rows + row) * dv + 4 * UNROLL * c;
+    const float* src = o_parts + (k * rows + row) * dv + 4 * c;
     f32x4 x[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) x[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
+    for (int u = 0; u < UNROLL; ++u)
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + 4 * tpr * u));
     if (l == kNegInf) continue;                 // an empty part changes nothing
     const float m_new = fmaxf(m, l);
     const float keep = fast_exp2((m - m_new) * kLog2e);   // 0 while m = -inf
@@ -63,9 +67,10 @@ lse_merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ ls
     if (OUT_BF16) {
       bf16x4 b = {static_cast<__bf16>(r[0]), static_cast<__bf16>(r[1]), static_cast<__bf16>(r[2]),
                   static_cast<__bf16>(r[3])};
-      *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(o_out) + row * dv + 4 * UNROLL * c + 4 * u) = b;
+      *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(o_out) + row * dv + 4 * c + 4 * tpr * u) = b;
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + row * dv + 4 * UNROLL * c + 4 * u) = r;
+      __builtin_nontemporal_store(r,
+                                  reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + row * dv + 4 * c + 4 * tpr * u));
     }
   }
   if (lse_out != nullptr && c == 0) lse_out[row] = lse;
