@@ -5,7 +5,8 @@ Each sampled row of attention depends only on its own query row and the keys
 visible to it, so the oracle evaluated on those rows is exact for them.
   C1  tiny non-causal ring, fp32: every row.
   C2  zigzag rank 0, seq 8192, cp 4: every row of 6 of the 32 heads, plus
-      the restore index bit for bit.
+      the restore index bit for bit; all four ranks gathered and restored
+      on the device: every row of 4 heads.
   C3  GQA decode over 8 shards, 64 x 131072: per-shard partials and merged
       output of 3 whole requests (all heads).
   C4  zigzag rank 0 of 1M tokens, cp 8: 512 (token, head) rows covering both
@@ -94,6 +95,37 @@ def test_c2_zigzag_full(ra):
                                       q_pos, np.arange(w["seq"]), causal=True)
         compare(o[:, h], lse[:, h], ro[0, :, 0], rl[0, :, 0], BF16_O, BF16_LSE, f"C2 head {h}")
     del w, graph
+    _release()
+
+
+def test_c2_every_rank_restored_on_device(ra):
+    """All four ranks of the 8192-token ring at full size (each in its own
+    ring order and step shapes), their outputs gathered in rank order and
+    put back in token order with the restore index on the device; every row
+    of 4 heads against full causal attention over the sequence."""
+    import workloads
+    outs_o, outs_l, restore = [], [], None
+    q_full = None
+    for r in range(4):
+        w = workloads.zigzag_setup(2, rank=r)
+        w["ring"].run(w["q_local"], w["o"], w["lse"])
+        outs_o.append(w["o"][0])
+        outs_l.append(w["lse"][0])
+        if q_full is None:
+            q_full = torch.empty((w["seq"], w["hq"], w["d"]), dtype=torch.bfloat16, device="cuda")
+            k_full, v_full, restore = w["k_full"][0], w["v_full"][0], w["restore"]
+        q_full[torch.as_tensor(np.asarray(w["local"]), device="cuda")] = w["q_local"][0]
+        say(f"C2 rank {r}: {w['q_local'].shape[1]} local tokens")
+    idx = torch.from_numpy(np.asarray(restore)).cuda()
+    o = ra.gather_rows(torch.cat(outs_o, 0), idx)
+    lse = ra.gather_rows(torch.cat(outs_l, 0), idx)
+    torch.cuda.synchronize()
+    seq = q_full.shape[0]
+    for h in (0, 9, 22, 31):
+        ro, rl = oracle.attention_ref(host64(q_full[None, :, h:h + 1]), host64(k_full[None, :, h:h + 1]),
+                                      host64(v_full[None, :, h:h + 1]), np.arange(seq), np.arange(seq), causal=True)
+        compare(host64(o[:, h]), host64(lse[:, h]), ro[0, :, 0], rl[0, :, 0], BF16_O, BF16_LSE,
+                f"C2 all ranks head {h}")
     _release()
 
 
