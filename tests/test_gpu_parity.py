@@ -707,6 +707,23 @@ def test_gather_rows_out_of_range_is_zero(ra):
         assert torch.equal(out[i], want)
 
 
+# (rows, bytes per row): more rows than the grid's 262,144 waves (waves loop
+# over rows); a row just past one 48 KiB burst per wave (a ragged second
+# round); rows of several bursts
+@pytest.mark.parametrize("n,row_bytes", [(300001, 16), (37, 48 * 1024 + 16), (5, 200 * 1024 + 48)])
+def test_gather_rows_bursts_and_grid_stride(ra, n, row_bytes):
+    say(f"gather rows n={n} row_bytes={row_bytes}")
+    g = torch.Generator(device="cuda").manual_seed(n)
+    src = torch.randint(-2**31, 2**31 - 1, (n, row_bytes // 4), dtype=torch.int32, device="cuda", generator=g)
+    idx = torch.randint(0, n, (n,), dtype=torch.int64, device="cuda", generator=g)
+    idx[0], idx[-1] = n - 1, -3                    # the last source row; one index out of range
+    out = ra.gather_rows(src, idx)
+    torch.cuda.synchronize()
+    want = src[idx.clamp(min=0)]
+    want[-1] = 0
+    assert torch.equal(out, want)
+
+
 # (q_len, k_len, q_pos0, k_pos0) of packed requests: self-causal, single
 # token, no queries, chunk tail over a long prefix, no keys, all keys later
 # (nothing visible), ragged tails past the tile size.
