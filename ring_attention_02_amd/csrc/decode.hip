@@ -10,12 +10,15 @@
 // gfx950 design: one workgroup (4 waves) per (shard, request, kv head, key
 // split).  The hq/hkv query heads of a kv head are packed into the 16
 // columns of v_mfma_f32_16x16x32_bf16, so K and V are streamed once per kv
-// head.  K goes from HBM straight into the A operand registers (each lane's
-// 64 contiguous bytes are exactly its operand), V goes through a per-wave LDS
-// slot and is read transposed with ds_read_b64_tr_b16.  Waves interleave on
-// 32-key tiles, prefetch one tile ahead, and their softmax states are merged
-// through LDS at the end; KV splits (only when there are too few work items
-// to fill the GPU) are merged by the LSE merge kernel.
+// head.  K and V are both read from HBM in whole 128-byte lines (16 lanes per
+// 256-byte row piece of a kv head), non-temporally, and go through per-wave
+// LDS slots: K is read back as the A operand with ds_read_b128, V transposed
+// with ds_read_b64_tr_b16.  (Loading K straight in the A operand's layout
+// reads half lines per instruction: a probe of this access pattern measured
+// 5.9 TB/s that way against 6.6 TB/s in whole non-temporal lines.)  Waves
+// interleave on 32-key tiles, prefetch one tile ahead, and their softmax
+// states are merged through LDS at the end; KV splits (only when there are
+// too few work items to fill the GPU) are merged by the LSE merge kernel.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -45,6 +48,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;          // keys per wave per round
 constexpr int kRound = kTile * kWaves;
 constexpr int kVPitch = kD + 32;   // bf16 per V row in LDS (+64 B: conflict-free transposed reads)
+constexpr int kKPitch = kD + 8;    // bf16 per K row in LDS (+16 B: conflict-free b128 reads)
 constexpr int kMaxGroup = 16;      // query heads per kv head that fit the MFMA columns
 constexpr int kTargetWgs = 2048;   // enough workgroups to fill 256 CUs several times
 
@@ -70,6 +74,8 @@ template <bool PAGED>
 __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) {
   // Per-wave V tile during the sweep; reused for the cross-wave merge.
   __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * kTile * kVPitch];
+  // Per-wave K tile during the sweep.
+  __shared__ __attribute__((aligned(16))) uint16_t ksmem[kWaves * kTile * kKPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,6 +117,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
 
   const int64_t row_stride = static_cast<int64_t>(a.hkv) * kD;  // elements between keys
   uint16_t* vslot = smem + wave * kTile * kVPitch;
+  uint16_t* kslot = ksmem + wave * kTile * kKPitch;
 
   // The wave's 32-key tile of round r: element offset of its first key (from
   // the K/V base) and how many of its keys exist (0 for a tile past the end
@@ -150,31 +157,23 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
     return t;
   };
 
-  // K: lane (key n16 of block kb, g) loads 64 contiguous bytes per block:
-  // kreg[kb*4 + c] = K[key][32c + 8g .. +7]  (the A operand of step c).
-  // V: lane loads rows 4i + g/... : vreg[i] = V[tile + 4i + lane/16][8*(lane%16) .. +7].
-  u32x4 kcur[8], knext[8], vnext[8];
-  auto load_k = [&](const Tile& t, u32x4* dst) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 16 + n16;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (key < t.valid) raw = *reinterpret_cast<const u32x4*>(a.k + t.off + key * row_stride + 32 * c + 8 * g);
-        dst[kb * 4 + c] = raw;
-      }
-    }
-  };
-  auto load_v = [&](const Tile& t) {
+  // K and V alike: lane loads rows 4i + g of the tile, 16 bytes at column
+  // 8 * (lane % 16): reg[i] = X[tile + 4i + lane/16][8*(lane%16) .. +7], so
+  // each instruction reads four whole 256-byte row pieces.  Rows past the
+  // tile's valid keys read as zero.
+  u32x4 knext[8], vnext[8];
+  auto load_rows = [&](const uint16_t* base, const Tile& t, u32x4* dst) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = 4 * i + g;
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (key < t.valid) raw = *reinterpret_cast<const u32x4*>(a.v + t.off + key * row_stride + 8 * n16);
-      vnext[i] = raw;
+      if (key < t.valid)
+        raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + t.off + key * row_stride + 8 * n16));
+      dst[i] = raw;
     }
   };
+  auto load_k = [&](const Tile& t) { load_rows(a.k, t, knext); };
+  auto load_v = [&](const Tile& t) { load_rows(a.v, t, vnext); };
 
   f32x4 oacc[8];
 #pragma unroll
@@ -185,18 +184,28 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   int32_t entry_now = entry_cur;     // entry of the round being computed
   if (rounds > 0) {
     const Tile t = tile_of(0, entry_cur);
-    load_k(t, kcur);
+    load_k(t);
     load_v(t);
   }
   for (int r = 0; r < rounds; ++r) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
       *reinterpret_cast<u32x4*>(&vslot[(4 * i + g) * kVPitch + 8 * n16]) = vnext[i];
+      *reinterpret_cast<u32x4*>(&kslot[(4 * i + g) * kKPitch + 8 * n16]) = knext[i];
+    }
     __syncthreads();
+    // A operand of step c for 16-key block kb: lane (key n16, g) holds
+    // K[kb*16 + n16][32c + 8g .. +7].
+    u32x4 kcur[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        kcur[kb * 4 + c] = *reinterpret_cast<const u32x4*>(&kslot[(kb * 16 + n16) * kKPitch + 32 * c + 8 * g]);
     if (r + 1 < rounds) {
       const Tile t = tile_of(r + 1, entry_next);
-      load_k(t, knext);
+      load_k(t);
       load_v(t);
     }
     const int valid = tile_of(r, entry_now).valid;
@@ -255,8 +264,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
                                                           0, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kcur[i] = knext[i];
   }
 
   // ---- merge the four waves' states through LDS
