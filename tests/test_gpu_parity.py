@@ -245,7 +245,7 @@ def test_segmented_prefill_small(ra):
     compare(host64(o), host64(lse), o_ref, lse_ref, BF16_O, BF16_LSE, "segmented")
 
 
-def _decode_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs=128, il=16):
+def _decode_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs=128, il=16, fill=0.0):
     d = 128
     tmax = max(ctx_lens)
     vbs = bs * n_shards
@@ -253,8 +253,9 @@ def _decode_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs=128, il=16):
     q, q64 = tensor(cfg, 1, 0, (B, hq, d), torch.bfloat16)
     k_ctx, k64 = tensor(cfg, 2, 0, (B, tmax, hkv, d), torch.bfloat16)
     v_ctx, v64 = tensor(cfg, 3, 0, (B, tmax, hkv, d), torch.bfloat16)
-    ks = torch.zeros((n_shards, B, t_shard, hkv, d), dtype=torch.bfloat16, device="cuda")
-    vs = torch.zeros_like(ks)
+    # rows past each shard's length hold `fill` (NaN: they must never be read)
+    ks = torch.full((n_shards, B, t_shard, hkv, d), fill, dtype=torch.bfloat16, device="cuda")
+    vs = torch.full_like(ks, fill)
     lens = np.zeros((n_shards, B), dtype=np.int64)
     for b, L in enumerate(ctx_lens):
         dev, slot = ra.slot_mapping(np.arange(L), bs, il, n_shards, 1)
@@ -291,6 +292,12 @@ def test_split_kv_decode_with_splits(ra):
 def test_split_kv_decode_group16_and_empty_shard(ra):
     say("decode: group 16, shard with no tokens")
     _decode_case(ra, 43, 2, [100, 2048], 8, 16, 1)
+
+
+def test_split_kv_decode_nan_past_shard_ends(ra):
+    # every K/V row past a shard's length is NaN; ragged last tiles everywhere
+    say("decode: NaN rows past every shard's end")
+    _decode_case(ra, 47, 3, [4096, 1500, 77], 8, 16, 2, fill=float("nan"))
 
 
 def test_zigzag_graph_replay_matches_eager(ra):
@@ -625,7 +632,7 @@ def test_jobs_random_diagonal_steps(ra, seed):
 
 
 def _decode_paged_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs, il, spare_blocks,
-                       drop=None):
+                       drop=None, fill=0.0):
     """Paged caches: each request has its own block table (a random choice of
     physical blocks, the same ids in every shard's pool, as the slot mapping
     places them); tokens go to pool[dev, table[vb] * bs + loc].  drop=(s, b, j)
@@ -642,8 +649,8 @@ def _decode_paged_case(ra, cfg, B, ctx_lens, n_shards, hq, hkv, bs, il, spare_bl
     q, q64 = tensor(cfg, 1, 0, (B, hq, d), torch.bfloat16)
     k_ctx, k64 = tensor(cfg, 2, 0, (B, tmax, hkv, d), torch.bfloat16)
     v_ctx, v64 = tensor(cfg, 3, 0, (B, tmax, hkv, d), torch.bfloat16)
-    kp = torch.zeros((n_shards, num_blocks, bs, hkv, d), dtype=torch.bfloat16, device="cuda")
-    vp = torch.zeros_like(kp)
+    kp = torch.full((n_shards, num_blocks, bs, hkv, d), fill, dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, fill)
     tables = np.full((n_shards, B, max_blocks), -1, dtype=np.int32)
     lens = np.zeros((n_shards, B), dtype=np.int64)
     devs, used = [], 0
@@ -694,6 +701,12 @@ def test_split_kv_decode_paged_splits_and_small_blocks(ra):
 def test_split_kv_decode_paged_entry_outside_pool(ra):
     say("paged decode: one table entry outside the pool is an empty block")
     _decode_paged_case(ra, 46, 2, [2048, 1000], 4, 8, 1, 64, 16, spare_blocks=3, drop=(1, 0, 2))
+
+
+def test_split_kv_decode_paged_nan_past_shard_ends(ra):
+    # pool rows no token occupies (block tails, spare blocks) are NaN
+    say("paged decode: NaN in every unoccupied pool row")
+    _decode_paged_case(ra, 48, 3, [4096, 1500, 77], 8, 16, 2, 128, 16, spare_blocks=5, fill=float("nan"))
 
 
 
