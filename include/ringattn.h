@@ -227,8 +227,9 @@ int32_t ring_attn_step(const void* q, const void* k, const void* v, int32_t dtyp
  * device passes its block on while it computes with it; [VID] chapter on
  * the wire budget: the transfer overlaps the step).  On one GPU the next
  * step's block is copied into the idle staging slot; the workgroups of the
- * attention launch each move a slice in their prologue, so no second
- * stream, event or copy kernel is needed.  dst / src are device pointers,
+ * attention launch each move a slice (half of them before their attention
+ * work, half after it), so no second stream, event or copy kernel is
+ * needed.  dst / src are device pointers,
  * 16-byte aligned, bytes a multiple of 16.  A dst range may overlap no
  * other forward range (src or dst) and no q / o / lse / k / v buffer of the
  * jobs, and a src range no o / lse buffer of the jobs (CP_EINVAL).  The
