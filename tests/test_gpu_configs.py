@@ -8,7 +8,8 @@ visible to it, so the oracle evaluated on those rows is exact for them.
       the restore index bit for bit; all four ranks gathered and restored
       on the device: every row of 4 heads.
   C3  GQA decode over 8 shards, 64 x 131072: per-shard partials and merged
-      output of 3 whole requests (all heads).
+      output of 3 whole requests (all heads), over contiguous shards and over
+      paged pools read through block tables.
   C4  zigzag rank 0 of 1M tokens, cp 8: 512 (token, head) rows covering both
       Q chunks, chunk edges, tile edges, the diagonal, and all 64 heads of a
       few tokens; rank 7 of the same ring (both query parts busy at every
@@ -147,6 +148,38 @@ def test_c3_decode_full(ra):
         compare(host64(o_parts[:, b]), host64(lse_parts[:, b]), po[:, 0], pl[:, 0], BF16_O,
                 BF16_LSE, f"C3 request {b} shard partials")
         compare(host64(o[b]), host64(lse[b]), mo[0], ml[0], BF16_O, BF16_LSE, f"C3 request {b}")
+    del w
+    _release()
+
+
+def test_c3_decode_paged_full(ra):
+    """C3 as benched in the paged layout: 8 pools of 128-token blocks, each
+    request's virtual blocks at a seeded random choice of physical blocks,
+    4,096 work items (no key splits: partials straight to o_parts).  Sampled
+    requests against the oracle, shard partials and merged result."""
+    import workloads
+    w = workloads.decode_paged_setup()
+    assert ra.split_kv_decode_workspace(w["n_shards"], w["B"], w["hq"], w["hkv"], w["d"],
+                                        w["tables"].shape[2] * w["kp"].shape[2]) == 0
+    o_parts, lse_parts = ra.split_kv_decode_paged(w["q"], w["kp"], w["vp"], w["tables"], w["lens"])
+    o, lse = ra.lse_merge(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    tables = w["tables"].cpu().numpy()
+    q64 = host64(w["q"])
+    for b in (0, 37, 63):
+        # the pools were filled through the library's slot mapping; the oracle's agrees
+        dev_ref, slot_ref = oracle.slot_mapping_ref(np.arange(w["ctx"]), 128, 16, 8, 1,
+                                                    block_table=tables[0, b])
+        dev, slot = ra.slot_mapping(np.arange(w["ctx"]), 128, 16, 8, 1, block_table=tables[0, b])
+        assert np.array_equal(dev, dev_ref) and np.array_equal(slot, slot_ref)
+        kc, vc = workloads.decode_context(b)
+        k64, v64 = host64(kc)[None], host64(vc)[None]
+        del kc, vc
+        po, pl, mo, ml = oracle.decode_shards_ref(q64[b:b + 1], k64, v64, dev_ref, w["n_shards"])
+        compare(host64(o_parts[:, b]), host64(lse_parts[:, b]), po[:, 0], pl[:, 0], BF16_O,
+                BF16_LSE, f"C3 paged request {b} shard partials")
+        compare(host64(o[b]), host64(lse[b]), mo[0], ml[0], BF16_O, BF16_LSE, f"C3 paged request {b}")
     del w
     _release()
 
