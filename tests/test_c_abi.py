@@ -77,3 +77,51 @@ def test_c_program_calls_the_host_entry_points(tmp_path):
     assert [int(x) for x in vals["reorg_dev_lens"]] == list(np.asarray(dev_lens).ravel())
 
     assert vals["status_string"][0].startswith("CP_EINVAL")
+
+
+@pytest.mark.gpu
+def test_c_program_runs_two_ring_steps_on_the_device(tmp_path):
+    """tests/c_abi_device.c: device memory from the HIP runtime, two
+    ring_attn_step calls (a FULL block, then a diagonal block merged in with
+    accumulate), no framework anywhere; the result against the oracle over
+    both blocks' keys."""
+    import seeded_inputs as si
+    from gpu_util import compare, say, BF16_O, BF16_LSE
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "c_abi_device")
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c_abi_device.c"), "-L", PKG, "-lringattn", f"-Wl,-rpath,{PKG}",
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-lm", "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    sq, ska, skb, hq, hkv, d = 200, 300, 150, 8, 2, 128
+    q_pos0, ka_pos0, kb_pos0 = 400, 0, 300
+    cfg = 61
+    q = si.normal_bf16_bits(cfg, 1, 0, (sq, hq, d))
+    ka = si.normal_bf16_bits(cfg, 2, 0, (ska, hkv, d))
+    va = si.normal_bf16_bits(cfg, 3, 0, (ska, hkv, d))
+    kb = si.normal_bf16_bits(cfg, 2, 1, (skb, hkv, d))
+    vb = si.normal_bf16_bits(cfg, 3, 1, (skb, hkv, d))
+    inp, outp = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        np.array([sq, ska, skb, hq, hkv, d, q_pos0, ka_pos0, kb_pos0, 1], dtype="<i8").tofile(f)
+        for a in (q, ka, va, kb, vb):
+            np.ascontiguousarray(a, dtype="<u2").tofile(f)
+    say(f"C program: two ring steps sq={sq} sk={ska}+{skb} hq={hq} hkv={hkv} d={d}")
+    res = subprocess.run([exe, str(inp), str(outp)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    raw = np.fromfile(outp, dtype=np.uint8)
+    o = raw[:4 * sq * hq * d].view("<f4").reshape(1, sq, hq, d)
+    lse = raw[4 * sq * hq * d:4 * sq * hq * (d + 1)].view("<f4").reshape(1, sq, hq)
+    cls = raw[4 * sq * hq * (d + 1):].view("<i4")
+    assert cls.tolist() == [oracle.classify_ref(q_pos0, sq, ka_pos0, ska, True),
+                            oracle.classify_ref(q_pos0, sq, kb_pos0, skb, True)] == [oracle.FULL, oracle.DIAG]
+    f64 = lambda bits: si.bf16_bits_to_f32(bits).astype(np.float64)[None]
+    k_all = np.concatenate([f64(ka), f64(kb)], 1)
+    v_all = np.concatenate([f64(va), f64(vb)], 1)
+    k_pos = np.concatenate([ka_pos0 + np.arange(ska), kb_pos0 + np.arange(skb)])
+    o_ref, lse_ref = oracle.attention_ref(f64(q), k_all, v_all, q_pos0 + np.arange(sq), k_pos, True)
+    compare(o, lse, o_ref, lse_ref, BF16_O, BF16_LSE, "C program, two ring steps")
